@@ -1,0 +1,244 @@
+"""Seeded synthetic inputs for one packed paged-attention step.
+
+This module only draws inputs: sequence lengths, block tables and N(0,1)
+values. It holds none of the step's arithmetic (no slots, no positions, no
+attention), so both the GPU path and the CPU oracle can consume what it
+makes without sharing any of the method.
+
+Recipe (shared by tests and the benchmark):
+  * one ``numpy.random.default_rng(seed)`` (PCG64) per step;
+  * draw order: lengths, then one permutation of the pool's block ids,
+    then cached-context K and V, then the step's new K and V, then Q;
+  * values are standard normal drawn in float32 and rounded
+    (round-to-nearest-even, by torch's CPU cast) to the step's dtype;
+  * integer lengths are uniform on inclusive ranges;
+  * sequence s needs ceil((c_s + n_s) / 16) blocks; block tables take
+    consecutive slices of the permutation, so physical placement is
+    random (tinyserve README "How it works": a sequence never owns a
+    contiguous cache region);
+  * with a shared prefix, the first ``prefix_blocks`` ids of the
+    permutation open every table and the prefix tokens have the same
+    values in every sequence (PageServe "03 Paged KV cache": full blocks
+    are shared between requests with a common prefix);
+  * padding entries of a block table are -1;
+  * packed token order is the sequence order given (the five named
+    configurations list decodes before prefill chunks, as tinyserve's
+    step orders decodes first, then chunked-prefill admissions).
+
+The five named configurations are Qwen2.5-shaped steps (see ``CONFIGS``).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+BLOCK_SIZE = 16
+
+_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass
+class Step:
+    """One packed step's inputs (all host memory)."""
+    name: str
+    seed: int
+    dtype: torch.dtype
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    num_blocks: int
+    num_layers: int
+    layer: int
+    block_size: int
+    q_lens: np.ndarray          # int32 [S]   new tokens per sequence this step
+    num_computed: np.ndarray    # int32 [S]   tokens whose K/V are already in the pool
+    block_tables: np.ndarray    # int32 [S, max_blocks], -1 padded
+    prefix_blocks: int          # blocks shared by every table (0: none)
+    k_ctx: Optional[torch.Tensor]  # [sum c_s, Hkv, D] cached context K, sequence after sequence
+    v_ctx: Optional[torch.Tensor]
+    k: Optional[torch.Tensor]      # [T, Hkv, D] this step's K
+    v: Optional[torch.Tensor]
+    q: Optional[torch.Tensor]      # [T, Hq, D]
+    scale: float
+
+    @property
+    def num_seqs(self) -> int:
+        return int(len(self.q_lens))
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q_lens.sum())
+
+    @property
+    def dtype_name(self) -> str:
+        return {v: k for k, v in _DTYPES.items()}[self.dtype]
+
+    def summary(self) -> dict:
+        return {"name": self.name, "dtype": self.dtype_name, "Hq": self.num_q_heads,
+                "Hkv": self.num_kv_heads, "D": self.head_dim, "S": self.num_seqs,
+                "T": self.num_tokens, "num_blocks": self.num_blocks,
+                "num_layers": self.num_layers, "layer": self.layer}
+
+
+def _normal(rng: np.random.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
+    a = rng.standard_normal(size=shape, dtype=np.float32)
+    t = torch.from_numpy(a)
+    return t if dtype == torch.float32 else t.to(dtype)
+
+
+def build_step(name: str, seed: int, dtype, num_q_heads: int, num_kv_heads: int,
+               head_dim: int, num_blocks: int, q_lens: Sequence[int],
+               num_computed: Sequence[int], *, rng: Optional[np.random.Generator] = None,
+               prefix_tokens: int = 0, num_layers: int = 1, layer: int = 0,
+               scale: Optional[float] = None, values: bool = True,
+               table_width: Optional[int] = None) -> Step:
+    """Draw block tables and values for the given lengths.
+
+    ``rng`` continues a generator that already drew the lengths; when None a
+    fresh one is seeded with ``seed``. ``prefix_tokens`` (a multiple of 16)
+    gives every sequence the same first blocks and the same values there.
+    """
+    if isinstance(dtype, str):
+        dtype = _DTYPES[dtype]
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    num_computed = np.asarray(num_computed, dtype=np.int32)
+    assert q_lens.shape == num_computed.shape
+    S = len(q_lens)
+    ctx = (num_computed.astype(np.int64) + q_lens)
+    assert prefix_tokens % BLOCK_SIZE == 0
+    prefix_blocks = prefix_tokens // BLOCK_SIZE
+    assert np.all(num_computed >= prefix_tokens), "prefix must lie in the cached context"
+
+    # blocks each sequence needs, and the permutation they are sliced from
+    nblk = [(int(c) + BLOCK_SIZE - 1) // BLOCK_SIZE for c in ctx]
+    width = max(nblk) if S else 1
+    if table_width is not None:
+        assert table_width >= width
+        width = table_width
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    need = prefix_blocks + sum(b - prefix_blocks for b in nblk)
+    assert need <= num_blocks, f"{name}: needs {need} blocks, pool has {num_blocks}"
+    tables = np.full((S, max(width, 1)), -1, dtype=np.int32)
+    off = prefix_blocks
+    for s in range(S):
+        tables[s, :prefix_blocks] = perm[:prefix_blocks]
+        own = nblk[s] - prefix_blocks
+        tables[s, prefix_blocks:nblk[s]] = perm[off:off + own]
+        off += own
+
+    k_ctx = v_ctx = k = v = q = None
+    T = int(q_lens.sum())
+    if values:
+        if prefix_tokens:
+            pk = _normal(rng, (prefix_tokens, num_kv_heads, head_dim), dtype)
+            pv = _normal(rng, (prefix_tokens, num_kv_heads, head_dim), dtype)
+            ks, vs = [], []
+            for s in range(S):
+                rest = int(num_computed[s]) - prefix_tokens
+                ks.append(torch.cat([pk, _normal(rng, (rest, num_kv_heads, head_dim), dtype)]))
+                vs.append(torch.cat([pv, _normal(rng, (rest, num_kv_heads, head_dim), dtype)]))
+            k_ctx = torch.cat(ks) if ks else pk[:0]
+            v_ctx = torch.cat(vs) if vs else pv[:0]
+        else:
+            nctx = int(num_computed.sum())
+            k_ctx = _normal(rng, (nctx, num_kv_heads, head_dim), dtype)
+            v_ctx = _normal(rng, (nctx, num_kv_heads, head_dim), dtype)
+        k = _normal(rng, (T, num_kv_heads, head_dim), dtype)
+        v = _normal(rng, (T, num_kv_heads, head_dim), dtype)
+        q = _normal(rng, (T, num_q_heads, head_dim), dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return Step(name=name, seed=seed, dtype=dtype, num_q_heads=num_q_heads,
+                num_kv_heads=num_kv_heads, head_dim=head_dim, num_blocks=num_blocks,
+                num_layers=num_layers, layer=layer, block_size=BLOCK_SIZE,
+                q_lens=q_lens, num_computed=num_computed, block_tables=tables,
+                prefix_blocks=prefix_blocks, k_ctx=k_ctx, v_ctx=v_ctx, k=k, v=v, q=q,
+                scale=float(scale))
+
+
+# ---------------------------------------------------------------------------
+# The five named configurations.
+
+def _c1(values=True):
+    # tiny fp32: 4 decodes at context 5, 17, 33, 50 and one 8-token prefill
+    # chunk at num_computed 0; 2 Q heads / 1 KV head, D 64, pool of 64 blocks
+    ctx = [5, 17, 33, 50]
+    q_lens = [1, 1, 1, 1, 8]
+    num_computed = [c - 1 for c in ctx] + [0]
+    return build_step("C1-tiny-fp32", 1, "f32", 2, 1, 64, 64, q_lens, num_computed,
+                      values=values)
+
+
+def _c2(values=True):
+    # Qwen2.5-0.5B-shaped decode step: 64 sequences, context U[16, 512]
+    rng = np.random.default_rng(2)
+    ctx = rng.integers(16, 512, size=64, endpoint=True)
+    return build_step("C2-qwen0.5b-decode-fp16", 2, "f16", 14, 2, 64, 4096,
+                      [1] * 64, (ctx - 1).tolist(), rng=rng, values=values)
+
+
+def _c3(values=True):
+    # Qwen2.5-1.5B-shaped mixed step: 128 decodes at context U[100, 2048]
+    # plus 4 prefill chunks of 512 at num_computed U[0, 1024]
+    rng = np.random.default_rng(3)
+    dctx = rng.integers(100, 2048, size=128, endpoint=True)
+    pc = rng.integers(0, 1024, size=4, endpoint=True)
+    q_lens = [1] * 128 + [512] * 4
+    num_computed = (dctx - 1).tolist() + pc.tolist()
+    return build_step("C3-qwen1.5b-mixed-fp16", 3, "f16", 12, 2, 128, 32768,
+                      q_lens, num_computed, rng=rng, values=values)
+
+
+def _c4(values=True):
+    # prefix sharing: 256 decodes whose first 1024 tokens (64 blocks) are the
+    # same physical blocks, then a private suffix of U[64, 512] tokens; the
+    # query is the last suffix token
+    rng = np.random.default_rng(4)
+    suffix = rng.integers(64, 512, size=256, endpoint=True)
+    ctx = 1024 + suffix
+    return build_step("C4-prefix-share-bf16", 4, "bf16", 12, 2, 128, 8192,
+                      [1] * 256, (ctx - 1).tolist(), rng=rng, prefix_tokens=1024,
+                      values=values)
+
+
+def _c5(values=True):
+    # long-context speculative verify: 32 sequences at context 32768 with
+    # 1 + 4 causal query tokens each, plus one 2048-token prefill chunk at
+    # position 30000
+    rng = np.random.default_rng(5)
+    q_lens = [5] * 32 + [2048]
+    num_computed = [32768 - 5] * 32 + [30000]
+    return build_step("C5-longctx-verify-bf16", 5, "bf16", 12, 2, 128, 80000,
+                      q_lens, num_computed, rng=rng, values=values)
+
+
+CONFIGS = {1: _c1, 2: _c2, 3: _c3, 4: _c4, 5: _c5}
+
+
+def config(idx: int, values: bool = True) -> Step:
+    """Named configuration ``idx`` in 1..5, seeded with ``idx``."""
+    return CONFIGS[idx](values=values)
+
+
+def random_step(seed: int, dtype="f16", num_q_heads=12, num_kv_heads=2, head_dim=128,
+                num_seqs=6, max_q=40, max_ctx=300, num_blocks=None, num_layers=1,
+                layer=0, values=True) -> Step:
+    """A small ragged step with mixed decode / verify / prefill sequences."""
+    rng = np.random.default_rng(seed)
+    q_lens = rng.integers(1, max_q, size=num_seqs, endpoint=True)
+    # a third of the sequences decode (1 token), a third verify (5 tokens)
+    kind = rng.integers(0, 3, size=num_seqs, endpoint=False)
+    q_lens = np.where(kind == 0, 1, np.where(kind == 1, np.minimum(5, max_q), q_lens))
+    num_computed = rng.integers(0, max_ctx, size=num_seqs, endpoint=True)
+    need = sum((int(c) + int(n) + 15) // 16 for c, n in zip(num_computed, q_lens))
+    if num_blocks is None:
+        num_blocks = 2 * need + 8
+    return build_step(f"random-{seed}", seed, dtype, num_q_heads, num_kv_heads, head_dim,
+                      num_blocks, q_lens.tolist(), num_computed.tolist(), rng=rng,
+                      num_layers=num_layers, layer=layer, values=values)
