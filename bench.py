@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Throughput of one packed paged-attention step on one MI355X.
+
+A step is the whole hot path over one batch of synthetic input: scatter
+this step's K/V into the block pool (ps_reshape_and_cache), then causal
+GQA attention of every packed query token through the block tables
+(ps_paged_attention: split-K decode/verify kernel, prefill-chunk kernel,
+split-K merge). The host planner's metadata is built and uploaded once
+before timing (inputs resident in HBM); its host cost is reported as
+``host_plan_us``.
+
+Default workload: the Qwen2.5-0.5B-shaped decode step (64 sequences,
+context U[16, 512], 14 Q / 2 KV heads, D 64, fp16). ``--config N`` picks
+another of the five named steps.
+
+The pool is replicated so that consecutive timed steps touch different
+copies and the working set exceeds the 256 MB Infinity Cache plus L2:
+every step reads its K/V from HBM, as a real step would.
+
+Prints one JSON line on stdout; details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA, TFLOP/s
+LLC_BYTES = 256 << 20          # Infinity Cache
+ROTATE_TARGET = 1 << 30        # bytes touched between reuses of one pool copy
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured FETCH/WRITE bytes per launch (from rocprofv3 --pmc), if present")
+    return ap.parse_args()
+
+
+def fill_context(P, step, pool, dev, stream):
+    """Write every sequence's cached context into the pool with the
+    library's own scatter (as the earlier steps that computed it would)."""
+    import numpy as np
+    import torch
+    kc, vc = step.k_ctx, step.v_ctx
+    offs = np.concatenate([[0], np.cumsum(step.num_computed.astype(np.int64))])
+    groups = []
+    if step.prefix_blocks:
+        # the shared prefix is written once, by the first sequence; the
+        # others only write their private part
+        P_tok = step.prefix_blocks * 16
+        groups.append(([0], [0], [int(step.num_computed[0])]))
+        rest = list(range(1, step.num_seqs))
+        groups.append((rest, [P_tok] * len(rest), [int(step.num_computed[s]) - P_tok for s in rest]))
+    else:
+        seqs = [s for s in range(step.num_seqs) if step.num_computed[s] > 0]
+        groups.append((seqs, [0] * len(seqs), [int(step.num_computed[s]) for s in seqs]))
+    for seqs, starts, lens in groups:
+        sel = [(s, a, n) for s, a, n in zip(seqs, starts, lens) if n > 0]
+        if not sel:
+            continue
+        rows = np.concatenate([np.arange(offs[s] + a, offs[s] + a + n) for s, a, n in sel])
+        idx = torch.from_numpy(rows)
+        kk = kc[idx].to(dev)
+        vv = vc[idx].to(dev)
+        ps = P.PackedStep([n for _, _, n in sel], [a for _, a, _ in sel],
+                          step.block_tables[[s for s, _, _ in sel]], step.num_q_heads, pool, dev,
+                          stream=stream)
+        ps.reshape_and_cache(kk, vv, pool, stream)
+        torch.cuda.synchronize()
+        del ps, kk, vv
+
+
+def cpu_baseline(step, seconds):
+    """The fp64 oracle (scatter + attention of the whole step) on host cores."""
+    import numpy as np
+    import torch
+    import oracle
+
+    def bits(t):
+        t = t.contiguous()
+        return t.view(torch.int32 if t.dtype == torch.float32 else torch.int16).numpy()
+
+    shape = (step.num_layers, step.num_blocks, 16, step.num_kv_heads, step.head_dim)
+    pk = np.zeros(shape, dtype=bits(step.k).dtype)
+    pv = np.zeros_like(pk)
+    kcb, vcb = bits(step.k_ctx), bits(step.v_ctx)
+    c0 = 0
+    for s in range(step.num_seqs):  # cached context, as the GPU pool holds it
+        c = int(step.num_computed[s])
+        oracle.store_tokens(pk, pv, step.layer, step.block_tables[s], 0, kcb[c0:c0 + c], vcb[c0:c0 + c])
+        c0 += c
+    q, kc, vc, k, v = (t.to(torch.float64).numpy() for t in (step.q, step.k_ctx, step.v_ctx, step.k, step.v))
+    kb, vb = bits(step.k), bits(step.v)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.reshape_and_cache(pk, pv, step.layer, kb, vb, step.q_lens, step.num_computed,
+                                 step.block_tables)
+        oracle.attention(q, kc, vc, k, v, step.q_lens, step.num_computed, step.scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 10000:
+            break
+    return {"value": round(reps * step.num_tokens / el, 3), "unit": "query tok/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} full steps of {step.name} (scatter + attention, fp64) in {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import paged_kv_attention_packed_amd as P
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    step = workloads.config(args.config)
+    log(f"workload {step.summary()}")
+
+    # ---- plan (host), timed separately
+    proto = P.ps_pool(0, 0, step.num_layers, step.num_blocks, 16, step.num_kv_heads,
+                      step.head_dim, P._binding.dtype_code(step.dtype), step.layer)
+    t0 = time.perf_counter()
+    nplan = 20
+    for _ in range(nplan):
+        P.ps_plan_step(step.q_lens, step.num_computed, step.block_tables, step.num_q_heads, proto)
+    host_plan_us = (time.perf_counter() - t0) / nplan * 1e6
+
+    # ---- pools: one filled copy, replicated
+    shape = (step.num_layers, step.num_blocks, 16, step.num_kv_heads, step.head_dim)
+    pk0 = torch.zeros(shape, dtype=step.dtype, device=dev)
+    pv0 = torch.zeros(shape, dtype=step.dtype, device=dev)
+    pool0 = P.make_pool(pk0, pv0, step.layer)
+    fill_context(P, step, pool0, dev, stream)
+
+    ps = P.PackedStep(step.q_lens, step.num_computed, step.block_tables, step.num_q_heads, pool0,
+                      dev, stream=stream)
+    info = ps.info
+    kv_bytes = info["kv_bytes_decode"] + info["kv_bytes_prefill"]
+    touched = info["kv_bytes_unique"] + info["q_bytes"] + info["out_bytes"] + info["scatter_bytes"]
+    pool_bytes = 2 * pk0.numel() * pk0.element_size()
+    nrot = max(1, math.ceil(ROTATE_TARGET / max(touched, 1)))
+    free = torch.cuda.mem_get_info()[0]
+    nrot = int(max(1, min(nrot, (free * 0.6) // pool_bytes)))
+    pools, tensors = [], []
+    for i in range(nrot):
+        if i == 0:
+            k_, v_ = pk0, pv0
+        else:
+            k_, v_ = pk0.clone(), pv0.clone()
+        tensors.append((k_, v_))
+        pools.append(P.make_pool(k_, v_, step.layer))
+    q = step.q.to(dev)
+    k = step.k.to(dev)
+    v = step.v.to(dev)
+    outs = [torch.empty_like(q) for _ in range(min(nrot, 8))]
+    torch.cuda.synchronize()
+    log(f"pool copies {nrot} x {pool_bytes / 2**20:.1f} MiB; touched/step {touched / 1e6:.2f} MB; "
+        f"plan {info}")
+
+    def one_step(i):
+        ps.run(q, k, v, pools[i % nrot], outs[i % len(outs)], step.scale, stream)
+
+    # ---- warmup, then the timed steps
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        one_step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- attention call alone (the dominant kernel(s)), same rotation
+    for i in range(args.warmup):
+        ps.attention(q, pools[i % nrot], outs[0], step.scale, stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        ps.attention(q, pools[i % nrot], outs[i % len(outs)], step.scale, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_attn = e0.elapsed_time(e1) / args.steps
+
+    # ---- scatter alone
+    e0.record(stream)
+    for i in range(args.steps):
+        ps.reshape_and_cache(k, v, pools[i % nrot], stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_scatter = e0.elapsed_time(e1) / args.steps
+
+    T = step.num_tokens
+    tok_s = T / (ms_step * 1e-3)
+    # algorithmic bytes of one attention call: each visible K/V row once per
+    # (sequence, KV head) -- physical blocks once when tables share them --
+    # plus q read, out write and block-table reads
+    attn_bytes = info["kv_bytes_unique"] + info["q_bytes"] + info["out_bytes"] + info["table_bytes"]
+    achieved = attn_bytes / (ms_attn * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            with open(args.traffic) as f:
+                tr = json.load(f).get(step.name)
+            traffic = tr["bytes_per_launch"] if tr else None
+        except (OSError, ValueError, KeyError):
+            traffic = None
+    flops = info["flops_decode"] + info["flops_prefill"]
+    kernels = ([f"ps_decode_kernel x{info['decode_items']}"] if info["decode_items"] else []) + \
+              ([f"ps_prefill_kernel x{info['prefill_items']}"] if info["prefill_items"] else []) + \
+              ([f"ps_merge_kernel x{info['merge_items']}"] if info["merge_items"] else [])
+
+    result = {
+        "metric": "packed paged-attn query tok/s + KV-read HBM GB/s (% peak), 1 MI355X",
+        "value": round(tok_s, 1),
+        "unit": "query tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16"}[step.dtype_name],
+        "data": "synthetic",
+        "config": {"workload": step.name, "num_seqs": step.num_seqs, "num_tokens": T,
+                   "num_q_heads": step.num_q_heads, "num_kv_heads": step.num_kv_heads,
+                   "head_dim": step.head_dim, "block_size": 16, "num_blocks": step.num_blocks,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "attention": {"call": "ps_paged_attention", "kernels": kernels,
+                      "algorithmic_bytes_per_launch": attn_bytes,
+                      "us_per_launch": round(ms_attn * 1e3, 3)},
+        "kv_read_gbs": round(kv_bytes / (ms_attn * 1e-3) / 1e9, 1),
+        "attention_tflops": round(flops / (ms_attn * 1e-3) / 1e12, 2),
+        "scatter_us": round(ms_scatter * 1e3, 3),
+        "host_plan_us": round(host_plan_us, 1),
+        "pool_copies": nrot,
+        "gpu": torch.cuda.get_device_name(0),
+        "torch": torch.__version__,
+        "hip": torch.version.hip,
+    }
+    try:
+        result["commit"] = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short", "HEAD"],
+                                          capture_output=True, text=True, timeout=5).stdout.strip() or None
+    except Exception:
+        result["commit"] = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline ...")
+        result["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)
+        result["cpu_baseline"]["cpu"] = platform.processor() or platform.machine()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,237 @@
+/*
+ * ps.h — C ABI of a packed paged-attention step for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * One scheduler step packs every scheduled token of every sequence into a
+ * single ragged [1, T] batch: prefill chunks, single decode tokens and
+ * speculative-verify rows (1 + k tokens) side by side (PageServe, "01
+ * Scheduler loop", Pack; "06 Development history", phase 8). The step
+ *   1. scatters this step's new K/V rows into a pre-allocated block pool
+ *      at slot = block_table[pos / 16] * 16 + pos % 16 (PageServe, "03
+ *      Paged KV cache", attention_wrapper code box), then
+ *   2. runs causal grouped-query attention for every packed query token
+ *      over its own sequence's context, reading K/V through the
+ *      sequence's block table (PageServe "03 Paged KV cache"; tinyserve
+ *      README "How it works": stepped causal mask over 1 + k rows).
+ *
+ * Conventions shared by every call:
+ *  - Device pointers are caller-owned (e.g. torch tensors); the library
+ *    never allocates or frees device memory. Host arrays are read during
+ *    the call only.
+ *  - A "stream" is a hipStream_t passed as void* (NULL = default stream).
+ *    Device work is enqueued asynchronously on it; the library never
+ *    synchronises. ps_paged_attention must be enqueued after
+ *    ps_reshape_and_cache of the same step on the same stream: attention
+ *    reads this step's K/V from the pool.
+ *  - Every call returns a ps_status. Argument errors are detected on the
+ *    host and returned before anything is enqueued. A launch failure
+ *    returns PS_ERR_HIP. ps_last_error_message() gives a readable reason
+ *    for the calling thread's last failure.
+ *  - No C++ exception crosses this boundary. Calls are reentrant; the
+ *    only global state is the per-thread error message.
+ *  - Supported: block_size 16; head_dim 64 or 128; fp32, fp16, bf16
+ *    storage with fp32 accumulation; num_q_heads a multiple of
+ *    num_kv_heads.
+ */
+#ifndef PS_H
+#define PS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PS_ABI_VERSION 1
+
+typedef int32_t ps_status;
+enum {
+    PS_OK = 0,
+    PS_ERR_INVALID_ARGUMENT = 1,    /* bad pointer, size, length or metadata */
+    PS_ERR_UNSUPPORTED = 2,         /* valid but not built: dtype, head_dim, block_size */
+    PS_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below ps_plan_sizes' figure */
+    PS_ERR_HIP = 4,                 /* the HIP runtime reported an error */
+    PS_ERR_HOST_MEMORY = 5          /* host allocation failed */
+};
+
+typedef enum { PS_F32 = 0, PS_F16 = 1, PS_BF16 = 2 } ps_dtype;
+
+/*
+ * The KV pool: two device arrays (K and V), each laid out
+ * [num_layers, num_blocks, block_size, num_kv_heads, head_dim] and
+ * contiguous (PageServe "06 Development history", phase 7: one pool
+ * [layers, blocks, 16, H, D]; tinyserve README "How it works": K and V in
+ * two slabs, H = number of KV heads). Every layer addresses the same block
+ * ids; `layer` picks the layer a call works on.
+ */
+typedef struct {
+    void *k;
+    void *v;
+    int32_t num_layers;
+    int32_t num_blocks;
+    int32_t block_size;   /* must be 16 */
+    int32_t num_kv_heads;
+    int32_t head_dim;     /* 64 or 128 */
+    int32_t dtype;        /* ps_dtype of K, V, Q and the output */
+    int32_t layer;        /* 0 <= layer < num_layers */
+} ps_pool;
+
+/*
+ * Opaque host object made by ps_plan_step: the step's metadata (the packed
+ * batch's index arrays) plus the kernels' work lists. One plan serves every
+ * layer of the step.
+ */
+typedef struct ps_plan ps_plan;
+
+/* ps_plan_step flags: which attention kernel serves each sequence. */
+enum {
+    PS_PLAN_DEFAULT = 0,      /* few query rows per KV head: split-K decode kernel; else prefill kernel */
+    PS_PLAN_ALL_DECODE = 1,   /* every sequence through the decode/verify kernel */
+    PS_PLAN_ALL_PREFILL = 2   /* every sequence through the prefill-chunk kernel */
+};
+
+/*
+ * Build the packed step's metadata on the host (the Pack stage of
+ * PageServe "01 Scheduler loop").
+ *
+ *   q_lens[num_seqs]               n_s >= 1: new tokens of sequence s this
+ *                                  step; they occupy rows
+ *                                  sum_{s'<s} n_s' .. +n_s-1 of the packed
+ *                                  batch, in sequence order
+ *   num_computed_tokens[num_seqs]  c_s >= 0: tokens of s whose K/V are
+ *                                  already in the pool (PageServe "01
+ *                                  Scheduler loop", System architecture).
+ *                                  Token i of s has position c_s + i.
+ *   block_tables[num_seqs * block_table_stride]
+ *                                  row s lists the physical blocks of s in
+ *                                  logical order; entries past
+ *                                  ceil((c_s + n_s) / 16) are ignored
+ *   num_q_heads                    query heads (a multiple of the pool's
+ *                                  num_kv_heads; head h reads KV head
+ *                                  h / (num_q_heads / num_kv_heads))
+ *   pool                           geometry and dtype (pointers unused here)
+ *   flags                          PS_PLAN_*
+ *
+ * Validates: lengths, table width, block ids in [0, num_blocks), no block
+ * twice in one table, distinct slots for the new tokens, and no new token
+ * written into a block that more than one table references (shared blocks
+ * are read-only; tinyserve README "How it works": copy-on-write precedes
+ * any write into a shared block). On success *out_plan owns host memory
+ * until ps_plan_destroy. num_seqs == 0 gives an empty plan.
+ */
+ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_computed_tokens,
+                       int32_t num_seqs, const int32_t *block_tables,
+                       int32_t block_table_stride, int32_t num_q_heads,
+                       const ps_pool *pool, uint32_t flags, ps_plan **out_plan);
+
+/*
+ * Device memory the caller must provide: metadata_bytes for
+ * ps_plan_upload (256-byte aligned), workspace_bytes for
+ * ps_paged_attention's split-K partial results (may be 0).
+ */
+ps_status ps_plan_sizes(const ps_plan *plan, size_t *metadata_bytes, size_t *workspace_bytes);
+
+/*
+ * Copy the plan's metadata into caller device memory metadata_dev
+ * (metadata_bytes long, 256-byte aligned) on `stream`. The plan remembers
+ * metadata_dev; that memory must stay valid, and unchanged, while the plan
+ * is used. The host copy stays owned by the plan, so the plan must outlive
+ * the copy (synchronise the stream before ps_plan_destroy).
+ */
+ps_status ps_plan_upload(ps_plan *plan, void *metadata_dev, size_t metadata_bytes, void *stream);
+
+/* Device addresses of the uploaded index arrays (valid after ps_plan_upload). */
+typedef struct {
+    const int32_t *slot_mapping;        /* [T]   flat slot of each packed token */
+    const int32_t *block_tables;        /* [S, block_table_stride] */
+    int32_t block_table_stride;
+    const int32_t *query_start_loc;     /* [S + 1] exclusive prefix sum of q_lens */
+    const int32_t *num_computed_tokens; /* [S] */
+    const int32_t *context_lens;        /* [S]   c_s + n_s */
+} ps_step_arrays;
+
+ps_status ps_plan_device_arrays(const ps_plan *plan, ps_step_arrays *arrays);
+
+/* Host copies of the same arrays (valid until ps_plan_destroy). */
+ps_status ps_plan_host_arrays(const ps_plan *plan, ps_step_arrays *arrays);
+
+/*
+ * What the step costs by definition (algorithmic work, not what a kernel
+ * happens to move). KV bytes count each visible (token, KV head) row of
+ * K and V once per sequence, shared by the query heads of its group; the
+ * "unique" figure counts each physical block once however many tables
+ * share it. flops = 4 * head_dim per (query row, visible key): one
+ * multiply-add each for q.k and for p.v.
+ */
+typedef struct {
+    int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, dtype;
+    int32_t decode_seqs, prefill_seqs;          /* sequences per attention kernel */
+    int32_t decode_items, prefill_items, merge_items;
+    int32_t decode_row_tiles;                   /* 16-row MFMA tiles per decode work item */
+    int64_t kv_bytes_decode, kv_bytes_prefill;  /* logical K+V bytes read */
+    int64_t kv_bytes_unique;                    /* distinct physical K+V bytes read */
+    int64_t q_bytes, out_bytes, scatter_bytes, table_bytes;
+    double flops_decode, flops_prefill;
+} ps_plan_info;
+
+ps_status ps_plan_get_info(const ps_plan *plan, ps_plan_info *info);
+
+void ps_plan_destroy(ps_plan *plan);
+
+/*
+ * Scatter this step's K/V into the pool (PageServe "01 Scheduler loop",
+ * Execute: writes K/V into the pool; "03 Paged KV cache": scatters new K/V
+ * into those slots). For t in [0, num_tokens):
+ *   pool.k[layer, slot/16, slot%16, :, :] = k[t, :, :]   (same for v)
+ * with slot = slot_mapping[t]. A byte copy.
+ *
+ *   k, v          device [num_tokens, num_kv_heads, head_dim], pool dtype
+ *   slot_mapping  device [num_tokens], distinct slots in [0, num_blocks*16);
+ *                 an entry outside that range is skipped
+ */
+ps_status ps_reshape_and_cache(const void *k, const void *v, const int32_t *slot_mapping,
+                               int32_t num_tokens, const ps_pool *pool, void *stream);
+
+/*
+ * Causal GQA attention of the packed step over the pool (PageServe "03
+ * Paged KV cache": attends through the table; tinyserve README
+ * "Highlights": grouped-query attention, "How it works": stepped causal
+ * mask). For packed token t = query_start_loc[s] + i of sequence s
+ * (position p = num_computed_tokens[s] + i) and query head h, with KV head
+ * j = h / (num_q_heads / num_kv_heads):
+ *   out[t, h, :] = sum_{tau <= p} softmax_tau(scale * q[t, h, :] . K_s[tau, j, :]) V_s[tau, j, :]
+ * where K_s[tau] is the pool row at block_tables[s][tau / 16], tau % 16.
+ * Softmax and accumulation run in fp32; the output is rounded to the pool
+ * dtype (round to nearest even).
+ *
+ *   q           device [num_tokens, num_q_heads, head_dim], pool dtype
+ *   block_tables, query_start_loc, num_computed_tokens, context_lens
+ *               device arrays with the contents ps_plan_step derived for
+ *               this step (e.g. those of ps_plan_device_arrays)
+ *   out         device [num_tokens, num_q_heads, head_dim], pool dtype
+ *   plan        the uploaded plan of this step; its sizes must match
+ *   workspace   device scratch of at least ps_plan_sizes' workspace_bytes
+ *               (256-byte aligned); the call overwrites it
+ */
+ps_status ps_paged_attention(const void *q, const ps_pool *pool,
+                             const int32_t *block_tables, int32_t block_table_stride,
+                             const int32_t *query_start_loc,
+                             const int32_t *num_computed_tokens,
+                             const int32_t *context_lens, void *out,
+                             int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                             float scale, const ps_plan *plan,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+const char *ps_status_string(ps_status status);
+
+/* Reason for the calling thread's last failed call ("" if none). */
+const char *ps_last_error_message(void);
+
+int32_t ps_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PS_H */

@@ -1,0 +1,13 @@
+"""Packed paged-attention step for AMD Instinct MI355X (gfx950).
+
+The work is done by ``libps.so`` (hand-written HIP kernels plus a C++ host
+planner behind the C ABI in ``include/ps.h``); this package is its Python
+binding plus a small helper that runs one step with torch-allocated device
+buffers.
+"""
+from ._binding import (  # noqa: F401
+    PS_BF16, PS_F16, PS_F32, PS_PLAN_ALL_DECODE, PS_PLAN_ALL_PREFILL, PS_PLAN_DEFAULT, Plan,
+    PsError, make_pool, ps_abi_version, ps_paged_attention, ps_plan_device_arrays,
+    ps_plan_get_info, ps_plan_host_arrays, ps_plan_sizes, ps_plan_step, ps_plan_upload,
+    ps_pool, ps_reshape_and_cache, status_string)
+from .step import PackedStep  # noqa: F401

@@ -1,0 +1,58 @@
+// C ABI glue: error reporting, status strings and the scatter entry point.
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "ps_internal.h"
+
+namespace {
+thread_local char g_err[512] = "";
+}
+
+ps_status ps_fail(ps_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+extern "C" const char *ps_last_error_message(void) { return g_err; }
+
+extern "C" const char *ps_status_string(ps_status status) {
+    switch (status) {
+        case PS_OK: return "ok";
+        case PS_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case PS_ERR_UNSUPPORTED: return "unsupported";
+        case PS_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case PS_ERR_HIP: return "HIP runtime error";
+        case PS_ERR_HOST_MEMORY: return "host memory exhausted";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int32_t ps_abi_version(void) { return PS_ABI_VERSION; }
+
+extern "C" ps_status ps_reshape_and_cache(const void *k, const void *v, const int32_t *slot_mapping,
+                                          int32_t num_tokens, const ps_pool *pool, void *stream) {
+    if (!pool) return ps_fail(PS_ERR_INVALID_ARGUMENT, "pool is NULL");
+    if (num_tokens < 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_tokens < 0");
+    if (pool->block_size != PS_BLOCK)
+        return ps_fail(PS_ERR_UNSUPPORTED, "block_size %d (only 16 is supported)", pool->block_size);
+    if (pool->head_dim != 64 && pool->head_dim != 128)
+        return ps_fail(PS_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", pool->head_dim);
+    if (pool->dtype != PS_F32 && pool->dtype != PS_F16 && pool->dtype != PS_BF16)
+        return ps_fail(PS_ERR_UNSUPPORTED, "dtype %d", pool->dtype);
+    if (pool->num_kv_heads < 1 || pool->num_layers < 1 || pool->num_blocks < 1)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "pool needs num_kv_heads, num_layers, num_blocks >= 1");
+    if (pool->layer < 0 || pool->layer >= pool->num_layers)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", pool->layer, pool->num_layers);
+    if ((int64_t)pool->num_blocks * PS_BLOCK > INT32_MAX)
+        return ps_fail(PS_ERR_UNSUPPORTED, "num_blocks %d: slots exceed int32", pool->num_blocks);
+    if (num_tokens == 0) return PS_OK;
+    if (!k || !v || !slot_mapping || !pool->k || !pool->v)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "a device pointer is NULL");
+    const int err = ps_launch_scatter(k, v, slot_mapping, num_tokens, pool, stream);
+    if (err != 0) return ps_fail(PS_ERR_HIP, "scatter launch: %s", ps_hip_error_string(err));
+    return PS_OK;
+}

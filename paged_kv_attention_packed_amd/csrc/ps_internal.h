@@ -1,0 +1,101 @@
+// Internal structures shared by the host planner and the HIP kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ps.h"
+
+// Rows of one attention work item are "packed rows" of one sequence and one
+// KV head: row r stands for query token r / g of the sequence and query head
+// kv_head * g + r % g (g = num_q_heads / num_kv_heads), so the g heads that
+// read the same K/V share every K/V load.
+struct ps_item {
+    int32_t seq;
+    int32_t kv_head;
+    int32_t row_begin;   // first packed row
+    int32_t row_end;     // one past the last packed row
+    int32_t key_begin;   // first key position (a multiple of 16)
+    int32_t key_end;     // one past the last key position (<= context length)
+    int32_t partial_row; // -1: write the output; else first workspace row of this item's partials
+    int32_t pad;
+};
+static_assert(sizeof(ps_item) == 32, "ps_item layout");
+
+// A set of split-K partials for the same rows, merged into the output.
+struct ps_merge {
+    int32_t seq;
+    int32_t kv_head;
+    int32_t row_begin;
+    int32_t row_end;
+    int32_t partial_row; // split i's rows start at partial_row + i * (row_end - row_begin)
+    int32_t num_splits;
+    int32_t pad0, pad1;
+};
+static_assert(sizeof(ps_merge) == 32, "ps_merge layout");
+
+// Tile geometry the planner and kernels agree on.
+constexpr int PS_BLOCK = 16;            // tokens per pool block
+constexpr int PS_DEC_TILE = 32;         // keys per decode-kernel wave iteration
+constexpr int PS_DEC_WAVES = 4;         // waves per decode work item
+constexpr int PS_DEC_MAX_ROWS = 32;     // packed rows per decode work item (two 16-row MFMA tiles)
+constexpr int PS_PRE_TILE = 64;         // keys per prefill LDS tile
+constexpr int PS_PRE_WAVES = 4;         // waves per prefill work item
+constexpr int PS_PRE_ROWS_PER_WAVE = 32;
+constexpr int PS_PRE_ROWS = PS_PRE_WAVES * PS_PRE_ROWS_PER_WAVE;  // 128 packed rows per prefill item
+
+// Workspace layout for split-K partials (all fp32):
+//   m[ws_rows]  running max (log2 domain), l[ws_rows] softmax denominator,
+//   acc[ws_rows][D] unnormalised output, d stored at position
+//   (d % (D/16)) * 16 + d / (D/16) (the order the MFMA epilogue holds it).
+inline size_t ps_align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct ps_ws_layout {
+    size_t off_m, off_l, off_acc, bytes;
+};
+
+inline ps_ws_layout ps_workspace_layout(int64_t ws_rows, int head_dim) {
+    ps_ws_layout w;
+    w.off_m = 0;
+    w.off_l = ps_align256(sizeof(float) * (size_t)ws_rows);
+    w.off_acc = w.off_l + ps_align256(sizeof(float) * (size_t)ws_rows);
+    w.bytes = ws_rows > 0 ? w.off_acc + ps_align256(sizeof(float) * (size_t)ws_rows * head_dim) : 0;
+    return w;
+}
+
+// Everything a launch needs, resolved from the plan and the call's arguments.
+struct ps_attn_launch {
+    const void *q;
+    void *out;
+    const void *pool_k;
+    const void *pool_v;
+    const int32_t *block_tables;
+    const int32_t *query_start_loc;
+    const int32_t *num_computed;
+    const int32_t *context_lens;
+    const ps_item *decode_items;
+    const ps_item *prefill_items;
+    const ps_merge *merges;
+    float *ws_m;
+    float *ws_l;
+    float *ws_acc;
+    int64_t layer_offset;   // elements from pool start to this layer
+    int32_t bt_stride;
+    int32_t num_blocks;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t dtype;
+    int32_t n_decode, n_prefill, n_merge;
+    int32_t decode_row_tiles;
+    float scale_log2;       // softmax scale * log2(e)
+};
+
+// Kernel launchers (ps_kernels.hip). Return hipError_t as int.
+int ps_launch_scatter(const void *k, const void *v, const int32_t *slot_mapping,
+                      int32_t num_tokens, const ps_pool *pool, void *stream);
+int ps_launch_attention(const ps_attn_launch &a, void *stream);
+const char *ps_hip_error_string(int err);
+
+// Set the calling thread's error message (ps_capi.cpp).
+ps_status ps_fail(ps_status st, const char *fmt, ...);

@@ -1,0 +1,451 @@
+// Host metadata builder for one packed step: validation, the packed batch's
+// index arrays, the attention kernels' work lists and the step's
+// algorithmic byte / FLOP counts. Pure host code: no HIP call happens here
+// except in ps_plan_upload.
+//
+// The packed layout follows PageServe "01 Scheduler loop" (Pack: one
+// [1, T] batch, explicit positions, a slot mapping per token, no padding)
+// and "03 Paged KV cache" (slot = block_table[pos / 16] * 16 + pos % 16).
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "ps_internal.h"
+
+struct ps_plan {
+    int32_t S = 0, T = 0, Hq = 0, Hkv = 0, D = 0, dtype = 0;
+    int32_t num_blocks = 0, num_layers = 0, bt_stride = 0;
+    uint32_t flags = 0;
+    int32_t dec_rt = 1;
+    int64_t ws_rows = 0;
+    int32_t n_dec = 0, n_pre = 0, n_mrg = 0;
+    // the metadata blob, laid out exactly as it is copied to the device
+    std::vector<uint8_t> blob;
+    size_t off_qsl = 0, off_nc = 0, off_ctx = 0, off_slot = 0, off_bt = 0;
+    size_t off_dec = 0, off_pre = 0, off_mrg = 0;
+    void *dev = nullptr;
+    ps_plan_info info{};
+
+    template <class X> X *host(size_t off) { return reinterpret_cast<X *>(blob.data() + off); }
+    template <class X> const X *host(size_t off) const {
+        return reinterpret_cast<const X *>(blob.data() + off);
+    }
+};
+
+namespace {
+
+int elt_bytes(int dtype) { return dtype == PS_F32 ? 4 : 2; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+int64_t env_int(const char *name, int64_t dflt) {
+    const char *s = std::getenv(name);
+    if (!s || !*s) return dflt;
+    char *end = nullptr;
+    long long v = std::strtoll(s, &end, 10);
+    return (end && *end == 0 && v > 0) ? (int64_t)v : dflt;
+}
+
+// Split [0, kmax) into near-equal pieces of about `target` keys, each a
+// multiple of `align` long except possibly the last. The split set depends
+// only on logical lengths, so physical placement never changes results.
+void key_splits(int64_t kmax, int64_t target, int64_t align, std::vector<int64_t> &bounds) {
+    bounds.clear();
+    int64_t n = std::max<int64_t>(1, ceil_div(kmax, target));
+    int64_t len = round_up(ceil_div(kmax, n), align);
+    n = ceil_div(kmax, len);
+    for (int64_t i = 0; i <= n; ++i) bounds.push_back(std::min(kmax, i * len));
+}
+
+}  // namespace
+
+extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_computed_tokens,
+                                  int32_t num_seqs, const int32_t *block_tables,
+                                  int32_t block_table_stride, int32_t num_q_heads,
+                                  const ps_pool *pool, uint32_t flags, ps_plan **out_plan) {
+    if (!out_plan) return ps_fail(PS_ERR_INVALID_ARGUMENT, "out_plan is NULL");
+    *out_plan = nullptr;
+    if (!pool) return ps_fail(PS_ERR_INVALID_ARGUMENT, "pool is NULL");
+    if (num_seqs < 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_seqs < 0");
+    if (num_seqs > 0 && (!q_lens || !num_computed_tokens || !block_tables))
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "q_lens, num_computed_tokens and block_tables must be non-NULL");
+    if (flags > PS_PLAN_ALL_PREFILL) return ps_fail(PS_ERR_INVALID_ARGUMENT, "unknown plan flags %u", flags);
+    if (pool->block_size != PS_BLOCK)
+        return ps_fail(PS_ERR_UNSUPPORTED, "block_size %d (only 16 is supported)", pool->block_size);
+    if (pool->head_dim != 64 && pool->head_dim != 128)
+        return ps_fail(PS_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", pool->head_dim);
+    if (pool->dtype != PS_F32 && pool->dtype != PS_F16 && pool->dtype != PS_BF16)
+        return ps_fail(PS_ERR_UNSUPPORTED, "dtype %d", pool->dtype);
+    if (pool->num_kv_heads < 1 || pool->num_layers < 1 || pool->num_blocks < 1)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "pool needs num_kv_heads, num_layers, num_blocks >= 1");
+    if (pool->layer < 0 || pool->layer >= pool->num_layers)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", pool->layer, pool->num_layers);
+    if ((int64_t)pool->num_blocks * PS_BLOCK > INT32_MAX)
+        return ps_fail(PS_ERR_UNSUPPORTED, "num_blocks %d: slots exceed int32", pool->num_blocks);
+    if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads != 0)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                       num_q_heads, pool->num_kv_heads);
+    if (num_seqs > 0 && block_table_stride < 1)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "block_table_stride %d < 1", block_table_stride);
+
+    const int32_t S = num_seqs;
+    const int32_t Hkv = pool->num_kv_heads, D = pool->head_dim, NB = pool->num_blocks;
+    const int32_t g = num_q_heads / Hkv;
+
+    // ---- per-sequence checks
+    int64_t T = 0;
+    for (int32_t s = 0; s < S; ++s) {
+        const int64_t n = q_lens[s], c = num_computed_tokens[s];
+        if (n < 1) return ps_fail(PS_ERR_INVALID_ARGUMENT, "q_lens[%d] = %lld < 1", s, (long long)n);
+        if (c < 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_computed_tokens[%d] = %lld < 0", s, (long long)c);
+        const int64_t ctx = c + n;
+        if (ctx > (int64_t)block_table_stride * PS_BLOCK)
+            return ps_fail(PS_ERR_INVALID_ARGUMENT,
+                           "sequence %d: context %lld needs %lld blocks, table width is %d", s,
+                           (long long)ctx, (long long)ceil_div(ctx, PS_BLOCK), block_table_stride);
+        if ((int64_t)g * n > INT32_MAX / 2 || ctx > INT32_MAX / 2)
+            return ps_fail(PS_ERR_UNSUPPORTED, "sequence %d too long", s);
+        T += n;
+    }
+    if (T > INT32_MAX / 2) return ps_fail(PS_ERR_UNSUPPORTED, "too many tokens (%lld)", (long long)T);
+
+    // ---- block ids, duplicates within a table, shared blocks
+    std::vector<int32_t> refs, seen;
+    try {
+        refs.assign(NB, 0);
+        seen.assign(NB, -1);
+    } catch (const std::bad_alloc &) {
+        return ps_fail(PS_ERR_HOST_MEMORY, "host allocation failed");
+    }
+    for (int32_t s = 0; s < S; ++s) {
+        const int32_t *row = block_tables + (int64_t)s * block_table_stride;
+        const int64_t nblk = ceil_div((int64_t)num_computed_tokens[s] + q_lens[s], PS_BLOCK);
+        for (int64_t b = 0; b < nblk; ++b) {
+            const int32_t id = row[b];
+            if (id < 0 || id >= NB)
+                return ps_fail(PS_ERR_INVALID_ARGUMENT, "block_tables[%d][%lld] = %d outside [0, %d)", s,
+                               (long long)b, id, NB);
+            if (seen[id] == s)
+                return ps_fail(PS_ERR_INVALID_ARGUMENT, "block %d appears twice in the table of sequence %d", id, s);
+            seen[id] = s;
+            refs[id] += 1;
+        }
+    }
+    for (int32_t s = 0; s < S; ++s) {
+        const int32_t *row = block_tables + (int64_t)s * block_table_stride;
+        const int64_t c = num_computed_tokens[s], ctx = c + q_lens[s];
+        for (int64_t b = c / PS_BLOCK; b < ceil_div(ctx, PS_BLOCK); ++b) {
+            if (refs[row[b]] > 1)
+                return ps_fail(PS_ERR_INVALID_ARGUMENT,
+                               "sequence %d writes new tokens into block %d, which %d tables share "
+                               "(copy it before writing)", s, row[b], refs[row[b]]);
+        }
+    }
+
+    ps_plan *p = new (std::nothrow) ps_plan();
+    if (!p) return ps_fail(PS_ERR_HOST_MEMORY, "host allocation failed");
+    p->S = S;
+    p->T = (int32_t)T;
+    p->Hq = num_q_heads;
+    p->Hkv = Hkv;
+    p->D = D;
+    p->dtype = pool->dtype;
+    p->num_blocks = NB;
+    p->num_layers = pool->num_layers;
+    p->bt_stride = S > 0 ? block_table_stride : 1;
+    p->flags = flags;
+
+    try {
+        // ---- work lists
+        std::vector<ps_item> dec, pre;
+        std::vector<ps_merge> mrg;
+        std::vector<char> is_dec(S);
+        for (int32_t s = 0; s < S; ++s) {
+            const int64_t rows = (int64_t)g * q_lens[s];
+            is_dec[s] = (flags == PS_PLAN_ALL_DECODE) ||
+                        (flags == PS_PLAN_DEFAULT && rows <= PS_DEC_MAX_ROWS);
+        }
+        // decode: a work item covers <= 32 packed rows and a slice of keys;
+        // slices are sized so the whole step yields a few thousand items
+        int64_t dec_keys = 0, pre_keys = 0, pre_tiles = 0;
+        for (int32_t s = 0; s < S; ++s) {
+            const int64_t rows = (int64_t)g * q_lens[s], c = num_computed_tokens[s];
+            const int64_t rb = is_dec[s] ? PS_DEC_MAX_ROWS : PS_PRE_ROWS;
+            for (int64_t r0 = 0; r0 < rows; r0 += rb) {
+                const int64_t r1 = std::min(rows, r0 + rb);
+                const int64_t kmax = c + (r1 - 1) / g + 1;
+                if (is_dec[s]) dec_keys += kmax * Hkv;
+                else { pre_keys += kmax * Hkv; pre_tiles += Hkv; }
+            }
+        }
+        const int64_t dec_split = env_int(
+            "PS_DECODE_SPLIT",
+            std::min<int64_t>(8192, std::max<int64_t>(128, round_up(ceil_div(dec_keys, 2048), 128))));
+        const int64_t pre_split = env_int(
+            "PS_PREFILL_SPLIT",
+            // only long key ranges are worth splitting: the partials of a
+            // 128-row tile cost as much traffic as ~500 keys of K/V
+            pre_tiles >= 256 ? INT32_MAX
+                             : std::max<int64_t>(4096, round_up(ceil_div(pre_keys, 512), PS_PRE_TILE)));
+
+        std::vector<int64_t> bounds;
+        int64_t ws_rows = 0;
+        int32_t dec_rt = 1;
+        for (int32_t s = 0; s < S; ++s) {
+            const int64_t rows = (int64_t)g * q_lens[s], c = num_computed_tokens[s];
+            const bool d = is_dec[s];
+            const int64_t rb = d ? PS_DEC_MAX_ROWS : PS_PRE_ROWS;
+            for (int32_t j = 0; j < Hkv; ++j) {
+                for (int64_t r0 = 0; r0 < rows; r0 += rb) {
+                    const int64_t r1 = std::min(rows, r0 + rb);
+                    const int64_t kmax = c + (r1 - 1) / g + 1;
+                    key_splits(kmax, d ? dec_split : pre_split, d ? PS_BLOCK : PS_PRE_TILE, bounds);
+                    const int64_t ns = (int64_t)bounds.size() - 1;
+                    if (d) dec_rt = std::max<int32_t>(dec_rt, (int32_t)ceil_div(r1 - r0, 16));
+                    const int64_t base = ns > 1 ? ws_rows : -1;
+                    for (int64_t i = 0; i < ns; ++i) {
+                        ps_item it{};
+                        it.seq = s;
+                        it.kv_head = j;
+                        it.row_begin = (int32_t)r0;
+                        it.row_end = (int32_t)r1;
+                        it.key_begin = (int32_t)bounds[i];
+                        it.key_end = (int32_t)bounds[i + 1];
+                        it.partial_row = ns > 1 ? (int32_t)(base + i * (r1 - r0)) : -1;
+                        (d ? dec : pre).push_back(it);
+                    }
+                    if (ns > 1) {
+                        ps_merge m{};
+                        m.seq = s;
+                        m.kv_head = j;
+                        m.row_begin = (int32_t)r0;
+                        m.row_end = (int32_t)r1;
+                        m.partial_row = (int32_t)base;
+                        m.num_splits = (int32_t)ns;
+                        mrg.push_back(m);
+                        ws_rows += ns * (r1 - r0);
+                    }
+                }
+            }
+        }
+        if (ws_rows > INT32_MAX / 2) {
+            delete p;
+            return ps_fail(PS_ERR_UNSUPPORTED, "split-K workspace too large");
+        }
+        p->dec_rt = dec_rt;
+        p->ws_rows = ws_rows;
+        p->n_dec = (int32_t)dec.size();
+        p->n_pre = (int32_t)pre.size();
+        p->n_mrg = (int32_t)mrg.size();
+
+        // ---- blob layout
+        size_t off = 0;
+        auto take = [&](size_t bytes) {
+            size_t o = off;
+            off = ps_align256(off + std::max<size_t>(bytes, 1));
+            return o;
+        };
+        p->off_qsl = take(sizeof(int32_t) * (S + 1));
+        p->off_nc = take(sizeof(int32_t) * S);
+        p->off_ctx = take(sizeof(int32_t) * S);
+        p->off_slot = take(sizeof(int32_t) * (size_t)T);
+        p->off_bt = take(sizeof(int32_t) * (size_t)S * p->bt_stride);
+        p->off_dec = take(sizeof(ps_item) * dec.size());
+        p->off_pre = take(sizeof(ps_item) * pre.size());
+        p->off_mrg = take(sizeof(ps_merge) * mrg.size());
+        p->blob.assign(off, 0);
+
+        int32_t *qsl = p->host<int32_t>(p->off_qsl);
+        int32_t *nc = p->host<int32_t>(p->off_nc);
+        int32_t *ctxl = p->host<int32_t>(p->off_ctx);
+        int32_t *slot = p->host<int32_t>(p->off_slot);
+        int32_t *bt = p->host<int32_t>(p->off_bt);
+        qsl[0] = 0;
+        for (int32_t s = 0; s < S; ++s) {
+            qsl[s + 1] = qsl[s] + q_lens[s];
+            nc[s] = num_computed_tokens[s];
+            ctxl[s] = num_computed_tokens[s] + q_lens[s];
+            const int32_t *row = block_tables + (int64_t)s * block_table_stride;
+            std::memcpy(bt + (int64_t)s * p->bt_stride, row, sizeof(int32_t) * p->bt_stride);
+            for (int32_t i = 0; i < q_lens[s]; ++i) {
+                const int64_t pos = (int64_t)nc[s] + i;
+                slot[qsl[s] + i] = row[pos / PS_BLOCK] * PS_BLOCK + (int32_t)(pos % PS_BLOCK);
+            }
+        }
+        if (!dec.empty()) std::memcpy(p->host<ps_item>(p->off_dec), dec.data(), sizeof(ps_item) * dec.size());
+        if (!pre.empty()) std::memcpy(p->host<ps_item>(p->off_pre), pre.data(), sizeof(ps_item) * pre.size());
+        if (!mrg.empty()) std::memcpy(p->host<ps_merge>(p->off_mrg), mrg.data(), sizeof(ps_merge) * mrg.size());
+
+        // ---- algorithmic accounting
+        ps_plan_info &I = p->info;
+        I.num_seqs = S;
+        I.num_tokens = (int32_t)T;
+        I.num_q_heads = num_q_heads;
+        I.num_kv_heads = Hkv;
+        I.head_dim = D;
+        I.dtype = pool->dtype;
+        I.decode_items = p->n_dec;
+        I.prefill_items = p->n_pre;
+        I.merge_items = p->n_mrg;
+        I.decode_row_tiles = dec_rt;
+        const int64_t e = elt_bytes(pool->dtype);
+        const int64_t row_kv = 2 * (int64_t)D * e;  // K + V bytes of one (token, KV head)
+        for (int32_t s = 0; s < S; ++s) {
+            const int64_t n = q_lens[s], c = num_computed_tokens[s], ctx = c + n;
+            const int64_t kvb = ctx * Hkv * row_kv;
+            const double fl = 4.0 * D * num_q_heads * ((double)n * c + 0.5 * (double)n * (n + 1));
+            if (is_dec[s]) { I.decode_seqs++; I.kv_bytes_decode += kvb; I.flops_decode += fl; }
+            else { I.prefill_seqs++; I.kv_bytes_prefill += kvb; I.flops_prefill += fl; }
+            I.table_bytes += 4 * ceil_div(ctx, PS_BLOCK);
+        }
+        // unique: each physical block once, with the most tokens any sharer reads
+        std::vector<int32_t> used(NB, 0);
+        for (int32_t s = 0; s < S; ++s) {
+            const int32_t *row = block_tables + (int64_t)s * block_table_stride;
+            const int64_t ctx = (int64_t)num_computed_tokens[s] + q_lens[s];
+            for (int64_t b = 0; b < ceil_div(ctx, PS_BLOCK); ++b)
+                used[row[b]] = std::max<int32_t>(used[row[b]], (int32_t)std::min<int64_t>(PS_BLOCK, ctx - b * PS_BLOCK));
+        }
+        for (int32_t b = 0; b < NB; ++b) I.kv_bytes_unique += (int64_t)used[b] * Hkv * row_kv;
+        I.q_bytes = T * num_q_heads * D * e;
+        I.out_bytes = I.q_bytes;
+        I.scatter_bytes = 2 * (T * Hkv * D * e) * 2 + 4 * T;
+    } catch (const std::bad_alloc &) {
+        delete p;
+        return ps_fail(PS_ERR_HOST_MEMORY, "host allocation failed");
+    }
+    *out_plan = p;
+    return PS_OK;
+}
+
+extern "C" ps_status ps_plan_sizes(const ps_plan *plan, size_t *metadata_bytes, size_t *workspace_bytes) {
+    if (!plan) return ps_fail(PS_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (metadata_bytes) *metadata_bytes = plan->blob.size();
+    if (workspace_bytes) *workspace_bytes = ps_workspace_layout(plan->ws_rows, plan->D).bytes;
+    return PS_OK;
+}
+
+extern "C" ps_status ps_plan_upload(ps_plan *plan, void *metadata_dev, size_t metadata_bytes, void *stream) {
+    if (!plan) return ps_fail(PS_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (!metadata_dev) return ps_fail(PS_ERR_INVALID_ARGUMENT, "metadata_dev is NULL");
+    if (((uintptr_t)metadata_dev & 255) != 0)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "metadata_dev is not 256-byte aligned");
+    if (metadata_bytes < plan->blob.size())
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "metadata buffer holds %zu bytes, plan needs %zu",
+                       metadata_bytes, plan->blob.size());
+    hipError_t e = hipMemcpyAsync(metadata_dev, plan->blob.data(), plan->blob.size(),
+                                  hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) return ps_fail(PS_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+    plan->dev = metadata_dev;
+    return PS_OK;
+}
+
+static void fill_arrays(const ps_plan *p, const uint8_t *base, ps_step_arrays *a) {
+    a->slot_mapping = reinterpret_cast<const int32_t *>(base + p->off_slot);
+    a->block_tables = reinterpret_cast<const int32_t *>(base + p->off_bt);
+    a->block_table_stride = p->bt_stride;
+    a->query_start_loc = reinterpret_cast<const int32_t *>(base + p->off_qsl);
+    a->num_computed_tokens = reinterpret_cast<const int32_t *>(base + p->off_nc);
+    a->context_lens = reinterpret_cast<const int32_t *>(base + p->off_ctx);
+}
+
+extern "C" ps_status ps_plan_device_arrays(const ps_plan *plan, ps_step_arrays *arrays) {
+    if (!plan || !arrays) return ps_fail(PS_ERR_INVALID_ARGUMENT, "plan or arrays is NULL");
+    if (!plan->dev) return ps_fail(PS_ERR_INVALID_ARGUMENT, "plan has not been uploaded");
+    fill_arrays(plan, static_cast<const uint8_t *>(plan->dev), arrays);
+    return PS_OK;
+}
+
+extern "C" ps_status ps_plan_host_arrays(const ps_plan *plan, ps_step_arrays *arrays) {
+    if (!plan || !arrays) return ps_fail(PS_ERR_INVALID_ARGUMENT, "plan or arrays is NULL");
+    fill_arrays(plan, plan->blob.data(), arrays);
+    return PS_OK;
+}
+
+extern "C" ps_status ps_plan_get_info(const ps_plan *plan, ps_plan_info *info) {
+    if (!plan || !info) return ps_fail(PS_ERR_INVALID_ARGUMENT, "plan or info is NULL");
+    *info = plan->info;
+    return PS_OK;
+}
+
+extern "C" void ps_plan_destroy(ps_plan *plan) { delete plan; }
+
+// ---------------------------------------------------------------------------
+// ps_paged_attention: argument checks against the plan, then the launches.
+
+extern "C" ps_status ps_paged_attention(const void *q, const ps_pool *pool,
+                                        const int32_t *block_tables, int32_t block_table_stride,
+                                        const int32_t *query_start_loc,
+                                        const int32_t *num_computed_tokens,
+                                        const int32_t *context_lens, void *out,
+                                        int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                        float scale, const ps_plan *plan,
+                                        void *workspace, size_t workspace_bytes, void *stream) {
+    if (!plan) return ps_fail(PS_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (!pool) return ps_fail(PS_ERR_INVALID_ARGUMENT, "pool is NULL");
+    if (num_seqs != plan->S || num_tokens != plan->T || num_q_heads != plan->Hq)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT,
+                       "call sizes (S=%d, T=%d, Hq=%d) differ from the plan's (S=%d, T=%d, Hq=%d)",
+                       num_seqs, num_tokens, num_q_heads, plan->S, plan->T, plan->Hq);
+    if (pool->num_kv_heads != plan->Hkv || pool->head_dim != plan->D || pool->dtype != plan->dtype ||
+        pool->num_blocks != plan->num_blocks || pool->num_layers != plan->num_layers ||
+        pool->block_size != PS_BLOCK)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "pool geometry differs from the plan's");
+    if (pool->layer < 0 || pool->layer >= pool->num_layers)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", pool->layer, pool->num_layers);
+    if (num_seqs > 0 && block_table_stride != plan->bt_stride)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "block_table_stride %d differs from the plan's %d",
+                       block_table_stride, plan->bt_stride);
+    if (!(scale > 0.0f) || !(scale < 1e30f))
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "scale must be positive and finite");
+    const ps_ws_layout wl = ps_workspace_layout(plan->ws_rows, plan->D);
+    if (workspace_bytes < wl.bytes)
+        return ps_fail(PS_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, step needs %zu",
+                       workspace_bytes, wl.bytes);
+    if (wl.bytes > 0 && (!workspace || ((uintptr_t)workspace & 255)))
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "workspace is NULL or not 256-byte aligned");
+    if (!plan->dev) return ps_fail(PS_ERR_INVALID_ARGUMENT, "plan has not been uploaded");
+    if (num_tokens == 0) return PS_OK;
+    if (!q || !out || !pool->k || !pool->v || !block_tables || !query_start_loc ||
+        !num_computed_tokens || !context_lens)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "a device pointer is NULL");
+
+    ps_attn_launch a{};
+    a.q = q;
+    a.out = out;
+    a.pool_k = pool->k;
+    a.pool_v = pool->v;
+    a.block_tables = block_tables;
+    a.query_start_loc = query_start_loc;
+    a.num_computed = num_computed_tokens;
+    a.context_lens = context_lens;
+    const uint8_t *dev = static_cast<const uint8_t *>(plan->dev);
+    a.decode_items = reinterpret_cast<const ps_item *>(dev + plan->off_dec);
+    a.prefill_items = reinterpret_cast<const ps_item *>(dev + plan->off_pre);
+    a.merges = reinterpret_cast<const ps_merge *>(dev + plan->off_mrg);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    a.ws_m = wl.bytes ? reinterpret_cast<float *>(ws + wl.off_m) : nullptr;
+    a.ws_l = wl.bytes ? reinterpret_cast<float *>(ws + wl.off_l) : nullptr;
+    a.ws_acc = wl.bytes ? reinterpret_cast<float *>(ws + wl.off_acc) : nullptr;
+    a.layer_offset = (int64_t)pool->layer * pool->num_blocks * PS_BLOCK * pool->num_kv_heads * pool->head_dim;
+    a.bt_stride = plan->bt_stride;
+    a.num_blocks = plan->num_blocks;
+    a.num_q_heads = plan->Hq;
+    a.num_kv_heads = plan->Hkv;
+    a.head_dim = plan->D;
+    a.dtype = plan->dtype;
+    a.n_decode = plan->n_dec;
+    a.n_prefill = plan->n_pre;
+    a.n_merge = plan->n_mrg;
+    a.decode_row_tiles = plan->dec_rt;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const int err = ps_launch_attention(a, stream);
+    if (err != 0) return ps_fail(PS_ERR_HIP, "attention launch: %s", ps_hip_error_string(err));
+    return PS_OK;
+}

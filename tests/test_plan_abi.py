@@ -1,0 +1,184 @@
+"""Host-side checks of the C ABI: exported symbols, the planner's packed
+metadata against the oracle's slot formula, validation errors, and the
+step's algorithmic byte / FLOP accounting. No GPU needed: nothing here
+launches a kernel or touches device memory."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_attention_packed_amd as P
+from paged_kv_attention_packed_amd import _binding as B
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DT = {"f32": P.PS_F32, "f16": P.PS_F16, "bf16": P.PS_BF16}
+
+
+def _pool(st, layer=None):
+    return P.ps_pool(0, 0, st.num_layers, st.num_blocks, 16, st.num_kv_heads, st.head_dim,
+                     DT[st.dtype_name], st.layer if layer is None else layer)
+
+
+def _plan(st, flags=0):
+    return P.ps_plan_step(st.q_lens, st.num_computed, st.block_tables, st.num_q_heads, _pool(st), flags)
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "ps.h")).read()
+    declared = set(re.findall(r"\b(ps_[a-z_]+)\s*\(", header))
+    assert declared == set(B.EXPORTED), declared ^ set(B.EXPORTED)
+    for name in declared:
+        assert hasattr(B.lib, name), name
+    assert P.ps_abi_version() == 1
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_planner_arrays_match_oracle_slot_formula(idx):
+    st = workloads.config(idx, values=False)
+    plan = _plan(st)
+    h = P.ps_plan_host_arrays(plan, st.num_seqs, st.num_tokens)
+    ql, nc = st.q_lens.astype(np.int64), st.num_computed.astype(np.int64)
+    np.testing.assert_array_equal(h["query_start_loc"], np.concatenate([[0], np.cumsum(ql)]))
+    np.testing.assert_array_equal(h["num_computed_tokens"], nc)
+    np.testing.assert_array_equal(h["context_lens"], nc + ql)
+    np.testing.assert_array_equal(h["block_tables"], st.block_tables)
+    expect = []
+    for s in range(st.num_seqs):
+        for i in range(int(ql[s])):
+            expect.append(oracle.slot(st.block_tables[s], int(nc[s]) + i))
+    np.testing.assert_array_equal(h["slot_mapping"], np.array(expect, dtype=np.int32))
+    assert len(set(expect)) == len(expect)
+
+
+def test_planner_slots_match_page_example():
+    # tinyserve README "How it works": seq A (19 tokens) [7, 2]; a step that
+    # appends A's tokens 16..18 writes slots 32, 33, 34 (block 2)
+    pool = P.ps_pool(0, 0, 1, 8, 16, 1, 64, P.PS_F16, 0)
+    plan = P.ps_plan_step([3], [16], np.array([[7, 2]]), 2, pool)
+    h = P.ps_plan_host_arrays(plan, 1, 3)
+    assert h["slot_mapping"].tolist() == [32, 33, 34]
+
+
+def test_algorithmic_accounting():
+    st = workloads.config(4, values=False)
+    info = P.ps_plan_get_info(_plan(st))
+    ctx = st.num_computed.astype(np.int64) + st.q_lens
+    row = 2 * st.head_dim * 2 * st.num_kv_heads           # K+V bytes per token, all KV heads (bf16)
+    assert info["kv_bytes_decode"] == int(ctx.sum()) * row
+    assert info["kv_bytes_prefill"] == 0
+    # unique: the 1024 shared prefix tokens count once
+    assert info["kv_bytes_unique"] == int((ctx - 1024).sum() + 1024) * row
+    T = st.num_tokens
+    assert info["q_bytes"] == T * st.num_q_heads * st.head_dim * 2
+    assert info["scatter_bytes"] == 2 * 2 * T * st.num_kv_heads * st.head_dim * 2 + 4 * T
+    assert info["flops_decode"] == pytest.approx(4 * st.head_dim * st.num_q_heads * float(ctx.sum()))
+    # a prefill chunk's flops: every row sees c + i + 1 keys
+    st5 = workloads.config(5, values=False)
+    i5 = P.ps_plan_get_info(_plan(st5))
+    n, c = 2048, 30000
+    assert i5["flops_prefill"] == pytest.approx(4 * 128 * 12 * (n * c + n * (n + 1) / 2))
+    assert i5["kv_bytes_decode"] == 2 ** 30
+
+
+def test_forced_paths_cover_every_sequence():
+    st = workloads.config(3, values=False)
+    dec = P.ps_plan_get_info(_plan(st, P.PS_PLAN_ALL_DECODE))
+    pre = P.ps_plan_get_info(_plan(st, P.PS_PLAN_ALL_PREFILL))
+    assert dec["prefill_seqs"] == 0 and dec["decode_seqs"] == st.num_seqs and dec["prefill_items"] == 0
+    assert pre["decode_seqs"] == 0 and pre["prefill_seqs"] == st.num_seqs and pre["decode_items"] == 0
+    dflt = P.ps_plan_get_info(_plan(st))
+    assert dflt["decode_seqs"] == 128 and dflt["prefill_seqs"] == 4
+
+
+def test_empty_step():
+    pool = P.ps_pool(0, 0, 1, 4, 16, 2, 128, P.PS_BF16, 0)
+    plan = P.ps_plan_step(np.zeros(0, np.int32), np.zeros(0, np.int32), np.zeros((0, 1), np.int32), 12, pool)
+    info = P.ps_plan_get_info(plan)
+    assert info["num_tokens"] == 0 and info["decode_items"] == 0 and info["prefill_items"] == 0
+    assert P.ps_plan_sizes(plan)[1] == 0
+
+
+def _expect_error(status, fn, *args, match=None, **kwargs):
+    with pytest.raises(P.PsError) as e:
+        fn(*args, **kwargs)
+    assert e.value.status == status
+    if match:
+        assert re.search(match, str(e.value)), str(e.value)
+
+
+def test_validation_errors():
+    pool = P.ps_pool(0, 0, 1, 8, 16, 2, 64, P.PS_F16, 0)
+    bt = np.array([[0, 1], [2, 3]], dtype=np.int32)
+    INV, UNS = B.PS_ERR_INVALID_ARGUMENT, B.PS_ERR_UNSUPPORTED
+    _expect_error(INV, P.ps_plan_step, [1, 0], [3, 3], bt, 4, pool, match="q_lens")
+    _expect_error(INV, P.ps_plan_step, [1, 1], [-1, 3], bt, 4, pool, match="num_computed")
+    _expect_error(INV, P.ps_plan_step, [1, 1], [3, 40], bt, 4, pool, match="table width")
+    _expect_error(INV, P.ps_plan_step, [1, 1], [3, 3], np.array([[0, 1], [9, 3]]), 4, pool, match="outside")
+    _expect_error(INV, P.ps_plan_step, [1, 1], [3, 20], np.array([[0, 1], [2, 2]]), 4, pool, match="twice")
+    # sequence 1 appends into block 0, which sequence 0 also reads
+    _expect_error(INV, P.ps_plan_step, [1, 1], [20, 3], np.array([[0, 1], [0, 3]]), 4, pool, match="share")
+    _expect_error(INV, P.ps_plan_step, [1, 1], [3, 3], bt, 5, pool, match="multiple")
+    _expect_error(INV, P.ps_plan_step, [1, 1], [3, 3], bt, 4, pool, 7, match="flags")
+    for field, val, st in [("head_dim", 96, UNS), ("block_size", 32, UNS), ("dtype", 7, UNS),
+                           ("layer", 1, INV), ("num_kv_heads", 0, INV)]:
+        bad = P.ps_pool(0, 0, 1, 8, 16, 2, 64, P.PS_F16, 0)
+        setattr(bad, field, val)
+        _expect_error(st, P.ps_plan_step, [1, 1], [3, 3], bt, 4, bad)
+    # a valid plan with reads of a shared block is fine
+    P.ps_plan_step([1, 1], [20, 20], np.array([[0, 1], [0, 3]]), 4, pool)
+
+
+def test_attention_argument_errors_return_before_any_launch():
+    st = workloads.config(2, values=False)
+    plan = _plan(st)
+    pool = _pool(st)
+    meta, ws = P.ps_plan_sizes(plan)
+    assert ws > 0
+    args = dict(q=1 << 20, pool=pool, block_tables=1 << 20, block_table_stride=st.block_tables.shape[1],
+                query_start_loc=1 << 20, num_computed_tokens=1 << 20, context_lens=1 << 20,
+                out=1 << 20, num_seqs=st.num_seqs, num_tokens=st.num_tokens,
+                num_q_heads=st.num_q_heads, scale=0.125, plan=plan, workspace=1 << 20,
+                workspace_bytes=ws)
+    INV = B.PS_ERR_INVALID_ARGUMENT
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        P.ps_paged_attention(**a)
+
+    _expect_error(INV, call, num_tokens=st.num_tokens + 1, match="differ")
+    _expect_error(INV, call, num_q_heads=7, match="differ")
+    _expect_error(INV, call, block_table_stride=3, match="stride")
+    _expect_error(B.PS_ERR_WORKSPACE_TOO_SMALL, call, workspace_bytes=ws - 1)
+    _expect_error(INV, call, scale=0.0, match="scale")
+    _expect_error(INV, call, scale=float("nan"), match="scale")
+    # everything consistent, but the plan was never uploaded
+    _expect_error(INV, call, match="uploaded")
+    bad = _pool(st)
+    bad.head_dim = 128
+    _expect_error(INV, call, pool=bad, match="geometry")
+
+
+def test_scatter_argument_errors():
+    pool = P.ps_pool(0, 0, 1, 8, 16, 2, 64, P.PS_F16, 0)
+    _expect_error(B.PS_ERR_INVALID_ARGUMENT, P.ps_reshape_and_cache, 1, 1, 1, -1, pool)
+    _expect_error(B.PS_ERR_INVALID_ARGUMENT, P.ps_reshape_and_cache, 0, 1, 1, 4, pool)
+    bad = P.ps_pool(0, 0, 1, 8, 8, 2, 64, P.PS_F16, 0)
+    _expect_error(B.PS_ERR_UNSUPPORTED, P.ps_reshape_and_cache, 1, 1, 1, 4, bad)
+    # zero tokens is a no-op even with NULL pointers
+    P.ps_reshape_and_cache(0, 0, 0, 0, pool)
+
+
+def test_split_plan_depends_only_on_logical_lengths():
+    a = workloads.config(3, values=False)
+    b = workloads.build_step("b", 77, "f16", 12, 2, 128, a.num_blocks, a.q_lens, a.num_computed,
+                             values=False)
+    pa, pb = _plan(a), _plan(b)
+    ia, ib = P.ps_plan_get_info(pa), P.ps_plan_get_info(pb)
+    for key in ("decode_items", "prefill_items", "merge_items"):
+        assert ia[key] == ib[key]
+    assert P.ps_plan_sizes(pa)[1] == P.ps_plan_sizes(pb)[1]
