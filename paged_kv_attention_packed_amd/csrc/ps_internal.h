@@ -43,11 +43,11 @@ constexpr int PS_PRE_TILE = 64;         // keys per prefill LDS tile
 constexpr int PS_PRE_WAVES = 4;         // waves per prefill work item
 constexpr int PS_PRE_ROWS_PER_WAVE = 32;
 constexpr int PS_PRE_ROWS = PS_PRE_WAVES * PS_PRE_ROWS_PER_WAVE;  // 128 packed rows per prefill item
+constexpr int PS_PRE_MAX_KEYS = 16384;  // keys per prefill item (its block ids are staged in LDS)
 
 // Workspace layout for split-K partials (all fp32):
 //   m[ws_rows]  running max (log2 domain), l[ws_rows] softmax denominator,
-//   acc[ws_rows][D] unnormalised output, d stored at position
-//   (d % (D/16)) * 16 + d / (D/16) (the order the MFMA epilogue holds it).
+//   acc[ws_rows][D] unnormalised output.
 inline size_t ps_align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct ps_ws_layout {

@@ -29,11 +29,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
 #include <type_traits>
 
 #include "ps_internal.h"
 
-namespace {
+namespace psk {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -85,13 +86,35 @@ __device__ inline f32x4 mfma4(float a, float b, f32x4 c) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over the 4 lanes l, l^16, l^32, l^48 (one packed row) with
+// the gfx950 row-swap permutes: permlane16_swap(x, x) leaves the pair
+// {x[l], x[l ^ 16]} in its two results, permlane32_swap the pair
+// {x[l], x[l ^ 32]}; both are VALU operations, unlike a ds_bpermute.
+__device__ inline void swap_pair16(float x, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    a = __builtin_bit_cast(float, r0);
+    b = __builtin_bit_cast(float, r1);
+}
+__device__ inline void swap_pair32(float x, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    a = __builtin_bit_cast(float, r0);
+    b = __builtin_bit_cast(float, r1);
+}
 __device__ inline float xor_max(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    float a, b;
+    swap_pair16(x, a, b);
+    swap_pair32(fmaxf(a, b), a, b);
+    return fmaxf(a, b);
 }
 __device__ inline float xor_sum(float x) {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    float a, b;
+    swap_pair16(x, a, b);
+    swap_pair32(a + b, a, b);
+    return a + b;
 }
 
 // N consecutive 32-bit words from a 4*N-byte aligned address
@@ -157,25 +180,52 @@ __device__ inline u32x4 v_operand(const uint32_t (&vr)[8][VW], int t) {
     return a;
 }
 
-// Online-softmax update of one row tile for 8*NSB scores already in
-// log2 units; returns the probabilities in pv.
-template <int NS>
-__device__ inline void softmax_update(float (&sv)[NS], float &m, float &l, float &alpha) {
-    float tmax = kNegInf;
+// Online-softmax update of one row tile from NS raw scores per lane
+// (masked scores are -inf). `c` = softmax scale * log2(e); m is the
+// reference max in log2 units, l the running denominator; on return sv
+// holds exp2(c * s - m). The reference only moves when some row's max
+// grows by more than 2^8 (then the accumulators are rescaled): the
+// numerator and denominator always share one reference, so the result is
+// the same softmax, with probabilities bounded by 256, and steady-state
+// tiles skip the rescale entirely. All row tiles of the wave share one
+// decision, so the rescale is a single uniform branch.
+constexpr float kLazyRescale = 8.f;
+
+template <int RT, int NS, int NT>
+__device__ inline void softmax_update(float (&sv)[RT][NS], float c, float (&m)[RT], float (&l)[RT],
+                                      f32x4 (&o)[RT][NT]) {
+    float tmax[RT];
+    bool grow = false;
 #pragma unroll
-    for (int e = 0; e < NS; ++e) tmax = fmaxf(tmax, sv[e]);
-    tmax = xor_max(tmax);
-    const float mnew = fmaxf(m, tmax);
-    const float muse = mnew == kNegInf ? 0.f : mnew;
-    alpha = fast_exp2(m - muse);
-    float psum = 0.f;
+    for (int rt = 0; rt < RT; ++rt) {
+        float x = kNegInf;
 #pragma unroll
-    for (int e = 0; e < NS; ++e) {
-        sv[e] = fast_exp2(sv[e] - muse);
-        psum += sv[e];
+        for (int e = 0; e < NS; ++e) x = fmaxf(x, sv[rt][e]);
+        tmax[rt] = xor_max(x) * c;
+        grow = grow || tmax[rt] > m[rt] + kLazyRescale;
     }
-    l = l * alpha + psum;
-    m = mnew;
+    if (__any(grow)) {  // one wave-uniform decision for all row tiles
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const float mnew = fmaxf(m[rt], tmax[rt]);
+            const float alpha = fast_exp2(m[rt] - (mnew == kNegInf ? 0.f : mnew));
+            l[rt] *= alpha;
+            m[rt] = mnew;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) o[rt][t] *= alpha;
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const float muse = m[rt] == kNegInf ? 0.f : m[rt];
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < NS; ++e) {
+            sv[rt][e] = fast_exp2(__builtin_fmaf(sv[rt][e], c, -muse));
+            psum += sv[rt][e];
+        }
+        l[rt] += psum;
+    }
 }
 
 // Which query row a lane's packed row stands for, its visibility limit and
@@ -307,25 +357,20 @@ __global__ __launch_bounds__(256, 2) void ps_decode_kernel(const ps_attn_launch 
             f32x4 sacc[2];
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) sacc[sb] = qk_tile<DT, D>(kf[buf][sb], qf[rt]);
+            const int vis = min(ke - 1, lim[rt]) - k0 - 4 * q4;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = k0 + sb * 16 + 4 * q4 + i;
-                    const float x = sacc[sb][i] * a.scale_log2;
-                    pv[rt][sb * 4 + i] = (key < ke && key <= lim[rt]) ? x : kNegInf;
-                }
-            float alpha;
-            softmax_update(pv[rt], m[rt], l[rt], alpha);
-#pragma unroll
-            for (int t = 0; t < NT; ++t) o[rt][t] *= alpha;
+                for (int i = 0; i < 4; ++i) pv[rt][sb * 4 + i] = sb * 16 + i <= vis ? sacc[sb][i] : kNegInf;
         }
+        softmax_update(pv, a.scale_log2, m, l, o);
         if (k0 + PS_DEC_TILE > ke) {
-            // ragged tile: V rows at or past key_end may be stale (even NaN)
-            // and P = 0 there would not cancel them
+            // V rows at or past key_end may be stale (even NaN) and P = 0
+            // there would not cancel them
+            const int vlim = ke - k0 - 4 * q4;
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
-                const bool ok = k0 + (jj >> 2) * 16 + 4 * q4 + (jj & 3) < ke;
+                const bool ok = (jj >> 2) * 16 + (jj & 3) < vlim;
 #pragma unroll
                 for (int w = 0; w < VW; ++w) vr[buf][jj][w] = ok ? vr[buf][jj][w] : 0u;
             }
@@ -426,10 +471,7 @@ __global__ __launch_bounds__(256, 2) void ps_decode_kernel(const ps_attn_launch 
     } else {
         const int64_t pr = (int64_t)it.partial_row + row;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const int d = d0 + e;
-            a.ws_acc[pr * D + (d % EPL) * 16 + d / EPL] = acc[e];
-        }
+        for (int e = 0; e < EPT; ++e) a.ws_acc[pr * D + d0 + e] = acc[e];
         if (d0 == 0) {
             a.ws_m[pr] = M;
             a.ws_l[pr] = L;
@@ -439,26 +481,106 @@ __global__ __launch_bounds__(256, 2) void ps_decode_kernel(const ps_attn_launch 
 
 // ---------------------------------------------------------------------------
 // Prefill-chunk attention. One workgroup = 128 packed rows (4 waves x 32)
-// of one sequence and KV head over a key slice. 64-key K and V tiles are
-// gathered through the block table into LDS (rows padded by 16 bytes so the
-// per-key fragment reads are bank-conflict free), the next tile's loads are
-// in flight in registers while the current one is consumed.
+// of one sequence and KV head over a key slice. K and V tiles (64 keys for
+// 16-bit data, 32 for fp32) are gathered through the block table straight
+// into LDS with global_load_lds_dwordx4 (no register staging) into a
+// two-stage ring, so the next tile streams in while the current one is
+// consumed. 16-byte chunks of each key row are XOR-swizzled by the row's
+// low 3 bits, which keeps the per-key K fragment reads and the per-row V
+// reads bank-conflict free without padding (the DMA writes whole 1 KiB
+// lines). Hand-offs use a bare s_barrier with explicit s_waitcnt, since a
+// fenced barrier would also wait for the tile still in flight.
 
-template <class DT, int D>
-__global__ __launch_bounds__(256, 2) void ps_prefill_kernel(const ps_attn_launch a) {
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// all waves reach this point with their LDS reads complete
+__device__ inline void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// one 16-byte global -> LDS DMA per lane; lane l lands at lds + 16 * l
+__device__ inline void dma16(const void *src, uint8_t *lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+#endif
+}
+
+// 16-byte chunk position of `chunk` in key row `row`: XOR-swizzled so that
+// 16 consecutive lanes reading one chunk of 16 consecutive rows, or 16
+// chunks of one row, touch 16 different 16-byte bank groups (256 bytes)
+//
+// 256-byte (and longer) rows: chunk ^ f(row), f a bijection of row % 16
+// that is even for each aligned group of 4 rows, so the transposed V reads
+// (2 adjacent chunks of 4 adjacent rows) also land in 8 distinct groups.
+template <int ROWB>
+__device__ inline int swz(int chunk, int row) {
+    if constexpr (ROWB >= 256) return chunk ^ (((row & 7) << 1) | ((row >> 3) & 1));
+    else return chunk ^ ((row >> 1) & 7);  // 128-byte rows: two rows share 256 bytes
+}
+
+// 4 16-bit values per lane, transposed within each 16-lane group: lane i
+// receives element i % 4 of the 8-byte loads issued by lanes 4e + i / 4,
+// e = 0..3
+__device__ inline u32x2 lds_read_tr16(const uint8_t *p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, r);
+#else
+    (void)p;
+    return u32x2{0u, 0u};
+#endif
+}
+
+// `bytes` bytes starting at byte `off` of swizzled LDS row `row`
+template <int ROWB, int VW>
+__device__ inline void lds_row_words(const uint8_t *rowp, int row, int off, uint32_t (&w)[VW]) {
+    if constexpr (VW == 2) {
+        const u32x2 x = *reinterpret_cast<const u32x2 *>(rowp + swz<ROWB>(off >> 4, row) * 16 + (off & 15));
+        w[0] = x[0];
+        w[1] = x[1];
+    } else {
+#pragma unroll
+        for (int i = 0; i < VW / 4; ++i) {
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(rowp + swz<ROWB>((off >> 4) + i, row) * 16);
+            w[4 * i + 0] = x[0];
+            w[4 * i + 1] = x[1];
+            w[4 * i + 2] = x[2];
+            w[4 * i + 3] = x[3];
+        }
+    }
+}
+
+// TK: keys per tile; OCC: waves per SIMD the register budget is sized for
+// (1: 512 registers, accumulators may live in AGPRs; 2: 256 registers)
+template <class DT, int D, int TK, int OCC>
+__global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_launch a) {
     using G = Geo<DT, D>;
     using T = typename DT::T;
     constexpr int ELT = G::ELT, KU4 = G::KU4, VW = G::VW, NT = G::NT, EPL = G::EPL;
     constexpr int RT = PS_PRE_ROWS_PER_WAVE / 16;
-    constexpr int TK = PS_PRE_TILE;
-    constexpr int ROWB = D * ELT + 16;        // LDS bytes per key row (padded)
-    constexpr int CPR = D * ELT / 16;         // 16-byte chunks per key row
-    constexpr int CPT = 2 * TK * CPR / 256;   // chunks per thread per K+V tile
     constexpr int NSB = TK / 16;
+    constexpr int ROWB = D * ELT;          // LDS bytes per key row
+    constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
+    constexpr int TILEB = TK * ROWB;       // one K (or V) tile
+    constexpr int STAGEB = 2 * TILEB;      // K then V
+    constexpr int NLD = STAGEB / 4096;     // 16-byte DMA loads per thread per stage
+    static_assert(CPR >= 8 && TILEB % 4096 == 0, "tile geometry");
+    static_assert(2 * PS_PRE_ROWS_PER_WAVE * D * ELT <= STAGEB, "output staging fits the ring");
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TK * ROWB];
-    uint8_t *const ksm = smem;
-    uint8_t *const vsm = smem + TK * ROWB;
+    // the two ring stages are separate objects so the compiler can tell a
+    // read of one from the DMA still filling the other
+    __shared__ __attribute__((aligned(1024))) uint8_t ring0[STAGEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring1[STAGEB];
+    __shared__ int32_t sbt[PS_PRE_MAX_KEYS / PS_BLOCK];  // the item's block ids
 
     const ps_item it = a.prefill_items[blockIdx.x];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -485,6 +607,13 @@ __global__ __launch_bounds__(256, 2) void ps_prefill_kernel(const ps_attn_launch
     for (int rt = 0; rt < RT; ++rt)
         load_q_row<DT, D>(a, wr0 + rt * 16 + c, it.row_end, g, j, qs0, nc, q4, qf[rt], lim[rt]);
 
+    // Block ids of the item's key range go to LDS once: inside the ring
+    // they could only be vector loads, and waiting for those would also
+    // wait for the tile in flight. Q is waited for here for the same reason.
+    for (int i = tid; i < (ke - kb + PS_BLOCK - 1) / PS_BLOCK; i += 256) sbt[i] = bt[(kb >> 4) + i];
+    wait_vmcnt<0>();
+    __syncthreads();
+
     float m[RT], l[RT];
     f32x4 o[RT][NT];
 #pragma unroll
@@ -495,80 +624,120 @@ __global__ __launch_bounds__(256, 2) void ps_prefill_kernel(const ps_attn_launch
         for (int t = 0; t < NT; ++t) o[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    u32x4 pf[CPT];
-    // one K+V tile = 4 pool blocks; their ids are scalar loads (k0 is
-    // uniform). Chunks of blocks past key_end read block 0 of the tile
-    // (always in bounds) and, like rows past key_end, are zeroed when the
-    // tile is stored to LDS, so the loads never wait on each other.
-    auto load_tile = [&](int k0) {
+    // DMA the K/V tile of keys [k0, k0 + TK) into ring stage `stage`. Block
+    // ids are scalar loads; keys of blocks past key_end re-read the tile's
+    // first block (in bounds) and are masked or zeroed at use.
+    constexpr int RPI = 4096 / ROWB;  // key rows one DMA instruction covers
+    static_assert(RPI >= 8 && (RPI <= 16 || RPI == 32), "rows per DMA instruction");
+    const int trow = tid / CPR;        // this thread's row within such a group
+    const int tpos = tid % CPR;        // and its 16-byte position in that row
+    auto issue_tile = [&](auto stagec, int k0) {
+        uint8_t *const ring = decltype(stagec)::value ? ring1 : ring0;
         int64_t blk[NSB];
-        blk[0] = bt[k0 >> 4];
+        const int b0 = (k0 - kb) >> 4;
+        blk[0] = __builtin_amdgcn_readfirstlane(sbt[b0]);
 #pragma unroll
-        for (int b = 1; b < NSB; ++b) blk[b] = (k0 + 16 * b < ke) ? (int64_t)bt[(k0 >> 4) + b] : blk[0];
+        for (int b = 1; b < NSB; ++b)
+            blk[b] = (k0 + 16 * b < ke) ? (int64_t)__builtin_amdgcn_readfirstlane(sbt[b0 + b]) : blk[0];
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int x = tid + i * 256;
-            const int kv = x / (TK * CPR);
-            const int rem = x - kv * (TK * CPR);
-            const int key = rem / CPR, ch = rem - key * CPR;
-            int64_t b = blk[0];
-#pragma unroll
-            for (int q = 1; q < NSB; ++q) b = (key >> 4) == q ? blk[q] : b;
-            const T *src = (kv ? vp : kp) + (b * 16 + (key & 15)) * rs;
-            pf[i] = reinterpret_cast<const u32x4 *>(src)[ch];
-        }
-    };
-    auto store_tile = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int x = tid + i * 256;
-            const int kv = x / (TK * CPR);
-            const int rem = x - kv * (TK * CPR);
-            const int key = rem / CPR, ch = rem - key * CPR;
-            *reinterpret_cast<u32x4 *>((kv ? vsm : ksm) + key * ROWB + ch * 16) =
-                (k0 + key < ke) ? pf[i] : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < NLD; ++i) {
+            const int r0 = (i * RPI) % TK;  // first key row of instruction i (compile-time)
+            const int kv = (i * RPI) / TK;  // K or V (compile-time)
+            const int key = r0 + trow;
+            int64_t b = blk[r0 >> 4];
+            if constexpr (RPI == 32) b = (trow >> 4) ? blk[(r0 >> 4) + 1] : b;
+            const int inblk = (key & 15) * (int)rs + swz<ROWB>(tpos, key) * (16 / ELT);
+            const T *src = (kv ? vp : kp) + b * 16 * rs + inblk;
+            dma16(src, ring + i * 4096 + wave * 1024);
         }
     };
 
-    auto compute_tile = [&](int k0) {
+    auto compute_tile = [&](auto stagec, int k0) {
+        const uint8_t *ksm = decltype(stagec)::value ? ring1 : ring0;
+        const uint8_t *vsm = ksm + TILEB;
         const bool full = (k0 + TK <= ke) && (k0 + TK - 1 <= lim_lo);
         f32x4 sacc[RT][NSB];
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
             u32x4 kf[KU4];
-            const uint8_t *kr = ksm + (sb * 16 + c) * ROWB + q4 * 16;
+            const uint8_t *kr = ksm + (sb * 16 + c) * ROWB;
 #pragma unroll
-            for (int u = 0; u < KU4; ++u) kf[u] = *reinterpret_cast<const u32x4 *>(kr + u * 64);
+            for (int u = 0; u < KU4; ++u) kf[u] = *reinterpret_cast<const u32x4 *>(kr + swz<ROWB>(u * 4 + q4, sb * 16 + c) * 16);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) sacc[rt][sb] = qk_tile<DT, D>(kf, qf[rt]);
         }
         float pv[RT][4 * NSB];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
+            // key k0 + sb*16 + 4*q4 + i is visible iff sb*16 + i <= vis
+            const int vis = min(ke - 1, lim[rt]) - k0 - 4 * q4;
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = sacc[rt][sb][i] * a.scale_log2;
-                    if (!full) {
-                        const int key = k0 + sb * 16 + 4 * q4 + i;
-                        x = (key < ke && key <= lim[rt]) ? x : kNegInf;
-                    }
-                    pv[rt][sb * 4 + i] = x;
-                }
-            float alpha;
-            softmax_update(pv[rt], m[rt], l[rt], alpha);
-#pragma unroll
-            for (int t = 0; t < NT; ++t) o[rt][t] *= alpha;
+                for (int i = 0; i < 4; ++i)
+                    pv[rt][sb * 4 + i] = (full || sb * 16 + i <= vis) ? sacc[rt][sb][i] : kNegInf;
         }
-        // P.V over two 32-key halves
+        softmax_update(pv, a.scale_log2, m, l, o);
+        // P.V over 32-key halves
+        if constexpr (ELT == 2) {
+            // A operand of O^T tile t straight from LDS with transposing
+            // reads: lane (c, q4) gets V[keys 4q4..4q4+3 and 16+4q4..19+4q4][d =
+            // 16t + c]; in the group the source lane j reads row (j / 4) of
+            // the key quad, d quad (j % 4)
+            const int j16 = lane & 15;
+            const int trow = 4 * q4 + (j16 >> 2);
+            const int tbyte = (j16 & 3) * 8;  // within a 32-byte d tile
+#pragma unroll
+            for (int h = 0; h < NSB / 2; ++h) {
+                const bool ragged = k0 + TK > ke;
+                u32x4 pb[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pb[rt][e] = pack2(pv[rt][8 * h + 2 * e], pv[rt][8 * h + 2 * e + 1], DT{});
+                const int r0 = 32 * h + trow, r1 = r0 + 16;
+                const uint8_t *v0 = vsm + r0 * ROWB, *v1 = vsm + r1 * ROWB;
+                // rows past key_end hold whatever the pool had: zero them.
+                // Element e of this lane's lo / hi words came from row
+                // 32h + 4q4 + e (+ 16 for hi).
+                u32x2 mlo = {~0u, ~0u}, mhi = {~0u, ~0u};
+                if (ragged) {
+                    const int vl = ke - k0 - 32 * h - 4 * q4;
+#pragma unroll
+                    for (int w = 0; w < 2; ++w) {
+                        mlo[w] = (2 * w < vl ? 0xFFFFu : 0u) | (2 * w + 1 < vl ? 0xFFFF0000u : 0u);
+                        mhi[w] = (16 + 2 * w < vl ? 0xFFFFu : 0u) | (17 + 2 * w < vl ? 0xFFFF0000u : 0u);
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int b = t * 32 + tbyte;
+                    u32x2 lo = lds_read_tr16(v0 + swz<ROWB>(b >> 4, r0) * 16 + (b & 15));
+                    u32x2 hi = lds_read_tr16(v1 + swz<ROWB>(b >> 4, r1) * 16 + (b & 15));
+                    if (ragged) {
+                        lo &= mlo;
+                        hi &= mhi;
+                    }
+                    const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) o[rt][t] = mfma32(av, pb[rt], o[rt][t], DT{});
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int h = 0; h < NSB / 2; ++h) {
             uint32_t vr[8][VW];
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 const int key = (2 * h + (jj >> 2)) * 16 + 4 * q4 + (jj & 3);
-                load_words<VW>(vsm + key * ROWB + EPL * c * ELT, vr[jj]);
+                lds_row_words<ROWB, VW>(vsm + key * ROWB, key, EPL * c * ELT, vr[jj]);
+                if (k0 + TK > ke) {  // rows past key_end hold whatever the pool had
+                    const bool ok = key < ke - k0;
+#pragma unroll
+                    for (int w = 0; w < VW; ++w) vr[jj][w] = ok ? vr[jj][w] : 0u;
+                }
             }
             if constexpr (ELT == 2) {
                 u32x4 pb[RT];
@@ -596,17 +765,30 @@ __global__ __launch_bounds__(256, 2) void ps_prefill_kernel(const ps_attn_launch
         }
     };
 
-    const int ntiles = (ke - kb + TK - 1) / TK;
-    if (ntiles > 0) load_tile(kb);
-    for (int ti = 0; ti < ntiles; ++ti) {
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    // tile ti sits in stage ti & 1; tile ti + 1 streams into the other
+    // stage while ti is consumed
+    // The last step re-reads its own tile into the idle stage instead of
+    // branching around the issue: a branch here would make the compiler
+    // wait for the in-flight tile before every LDS read.
+    auto step = [&](auto cur, auto nxt, int ti, int ntiles) {
         const int k0 = kb + ti * TK;
-        __syncthreads();
-        store_tile(k0);
-        __syncthreads();
-        if (ti + 1 < ntiles) load_tile(k0 + TK);
-        if (active && k0 <= lim_hi) compute_tile(k0);
+        issue_tile(nxt, ti + 1 < ntiles ? k0 + TK : k0);
+        wait_vmcnt<NLD>();  // this thread's loads of tile ti have landed
+        lds_barrier();      // ... and every other thread's
+        if (active && k0 <= lim_hi) compute_tile(cur, k0);
+        lds_barrier();  // stage `cur` is free for tile ti + 2
+    };
+    const int ntiles = (ke - kb + TK - 1) / TK;
+    if (ntiles > 0) issue_tile(S0{}, kb);
+    for (int ti = 0; ti < ntiles; ti += 2) {
+        step(S0{}, S1{}, ti, ntiles);
+        if (ti + 1 < ntiles) step(S1{}, S0{}, ti + 1, ntiles);
     }
 
+    wait_vmcnt<0>();  // the last, unused tile must land before the ring is reused
+    __syncthreads();
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) l[rt] = xor_sum(l[rt]);
 
@@ -618,7 +800,14 @@ __global__ __launch_bounds__(256, 2) void ps_prefill_kernel(const ps_attn_launch
             if (r >= it.row_end) continue;
             const int64_t pr = (int64_t)it.partial_row + (r - it.row_begin);
 #pragma unroll
-            for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4 *>(a.ws_acc + pr * D + t * 16 + 4 * q4) = o[rt][t];
+            for (int t = 0; t < NT; ++t) {
+                if constexpr (ELT == 2) {  // tile t row 4q4 + i holds d = 16t + 4q4 + i
+                    *reinterpret_cast<f32x4 *>(a.ws_acc + pr * D + t * 16 + 4 * q4) = o[rt][t];
+                } else {                   // ... d = EPL (4q4 + i) + t
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) a.ws_acc[pr * D + EPL * (4 * q4 + i) + t] = o[rt][t][i];
+                }
+            }
             if (q4 == 0) {
                 a.ws_m[pr] = m[rt];
                 a.ws_l[pr] = l[rt];
@@ -628,8 +817,7 @@ __global__ __launch_bounds__(256, 2) void ps_prefill_kernel(const ps_attn_launch
     }
 
     // final output: normalise, round, transpose through LDS, write rows
-    __syncthreads();
-    T *so = reinterpret_cast<T *>(smem) + wave * PS_PRE_ROWS_PER_WAVE * D;
+    T *so = reinterpret_cast<T *>(wave < 2 ? ring0 : ring1) + (wave & 1) * PS_PRE_ROWS_PER_WAVE * D;
     if (active) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -637,15 +825,18 @@ __global__ __launch_bounds__(256, 2) void ps_prefill_kernel(const ps_attn_launch
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    so[(rt * 16 + c) * D + EPL * (4 * q4 + i) + t] = cvt_out(o[rt][t][i] * inv, DT{});
+                for (int i = 0; i < 4; ++i) {
+                    const int d = ELT == 2 ? 16 * t + 4 * q4 + i : EPL * (4 * q4 + i) + t;
+                    so[(rt * 16 + c) * D + d] = cvt_out(o[rt][t][i] * inv, DT{});
+                }
         }
     }
     __syncthreads();
     if (!active) return;
+    constexpr int OCPR = D * ELT / 16;
     const uint8_t *sob = reinterpret_cast<const uint8_t *>(so);
-    for (int x = lane; x < PS_PRE_ROWS_PER_WAVE * CPR; x += 64) {
-        const int row = x / CPR, ch = x - row * CPR;
+    for (int x = lane; x < PS_PRE_ROWS_PER_WAVE * OCPR; x += 64) {
+        const int row = x / OCPR, ch = x - row * OCPR;
         const int r = wr0 + row;
         if (r >= it.row_end) continue;
         const int tok = r / g;
@@ -661,7 +852,6 @@ __global__ __launch_bounds__(256, 2) void ps_prefill_kernel(const ps_attn_launch
 template <class DT, int D>
 __global__ __launch_bounds__(256) void ps_merge_kernel(const ps_attn_launch a) {
     using T = typename DT::T;
-    constexpr int EPL = D / 16;
     constexpr int CH = 8;
     const ps_merge mg = a.merges[blockIdx.x];
     const int rows = mg.row_end - mg.row_begin;
@@ -680,11 +870,14 @@ __global__ __launch_bounds__(256) void ps_merge_kernel(const ps_attn_launch a) {
             const int64_t pr = (int64_t)mg.partial_row + (int64_t)sp * rows + row;
             const float f = fast_exp2(a.ws_m[pr] - muse);
             L += a.ws_l[pr] * f;
-            const float *ap = a.ws_acc + pr * D;
+            const f32x4 *ap = reinterpret_cast<const f32x4 *>(a.ws_acc + pr * D + d0);
 #pragma unroll
-            for (int e = 0; e < CH; ++e) {
-                const int d = d0 + e;
-                acc[e] += ap[(d % EPL) * 16 + d / EPL] * f;
+            for (int e = 0; e < CH / 4; ++e) {
+                const f32x4 x = ap[e];
+                acc[4 * e + 0] += x[0] * f;
+                acc[4 * e + 1] += x[1] * f;
+                acc[4 * e + 2] += x[2] * f;
+                acc[4 * e + 3] += x[3] * f;
             }
         }
         const int r = mg.row_begin + row;
@@ -700,6 +893,18 @@ __global__ __launch_bounds__(256) void ps_merge_kernel(const ps_attn_launch a) {
 // ---------------------------------------------------------------------------
 // Launchers
 
+// Prefill kernel shape (tuning knob, PS_PREFILL_VARIANT): 0 = 64-key tiles
+// (32 for fp32) at two waves per SIMD (default), 1 = the same tiles with a
+// 512-register budget at one wave per SIMD, 2 = 32-key tiles at two waves
+// per SIMD.
+int prefill_variant() {
+    static const int v = [] {
+        const char *e = std::getenv("PS_PREFILL_VARIANT");
+        return e ? std::atoi(e) : 0;
+    }();
+    return v;
+}
+
 template <class DT, int D>
 hipError_t launch_attention_t(const ps_attn_launch &a, hipStream_t st) {
     if (a.n_decode > 0) {
@@ -708,8 +913,22 @@ hipError_t launch_attention_t(const ps_attn_launch &a, hipStream_t st) {
         else
             hipLaunchKernelGGL((ps_decode_kernel<DT, D, 2>), dim3(a.n_decode), dim3(256), 0, st, a);
     }
-    if (a.n_prefill > 0)
-        hipLaunchKernelGGL((ps_prefill_kernel<DT, D>), dim3(a.n_prefill), dim3(256), 0, st, a);
+    if (a.n_prefill > 0) {
+        constexpr int TK = DT::ELT == 2 ? PS_PRE_TILE : PS_PRE_TILE / 2;
+        switch (prefill_variant()) {
+            case 1:
+                hipLaunchKernelGGL((ps_prefill_kernel<DT, D, TK, 1>), dim3(a.n_prefill), dim3(256), 0, st, a);
+                break;
+            case 2:
+                if constexpr (TK != 32) {  // (for fp32 this is the default shape)
+                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, 32, 2>), dim3(a.n_prefill), dim3(256), 0, st, a);
+                    break;
+                }
+                [[fallthrough]];
+            default:
+                hipLaunchKernelGGL((ps_prefill_kernel<DT, D, TK, 2>), dim3(a.n_prefill), dim3(256), 0, st, a);
+        }
+    }
     if (a.n_merge > 0)
         hipLaunchKernelGGL((ps_merge_kernel<DT, D>), dim3(a.n_merge), dim3(256), 0, st, a);
     return hipGetLastError();
@@ -720,7 +939,9 @@ hipError_t launch_attention_d(const ps_attn_launch &a, hipStream_t st) {
     return a.head_dim == 64 ? launch_attention_t<DT, 64>(a, st) : launch_attention_t<DT, 128>(a, st);
 }
 
-}  // namespace
+}  // namespace psk
+
+using namespace psk;
 
 int ps_launch_attention(const ps_attn_launch &a, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -205,7 +205,8 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                 for (int64_t r0 = 0; r0 < rows; r0 += rb) {
                     const int64_t r1 = std::min(rows, r0 + rb);
                     const int64_t kmax = c + (r1 - 1) / g + 1;
-                    key_splits(kmax, d ? dec_split : pre_split, d ? PS_BLOCK : PS_PRE_TILE, bounds);
+                    key_splits(kmax, d ? dec_split : std::min<int64_t>(pre_split, PS_PRE_MAX_KEYS),
+                               d ? PS_BLOCK : PS_PRE_TILE, bounds);
                     const int64_t ns = (int64_t)bounds.size() - 1;
                     if (d) dec_rt = std::max<int32_t>(dec_rt, (int32_t)ceil_div(r1 - r0, 16));
                     const int64_t base = ns > 1 ? ws_rows : -1;
