@@ -22,16 +22,20 @@ struct ps_item {
 };
 static_assert(sizeof(ps_item) == 32, "ps_item layout");
 
-// A set of split-K partials for the same rows, merged into the output.
+// A chunk of rows (at most ps_merge_rows(D)) of one set of split-K
+// partials, merged into the output by one workgroup of the merge kernel.
 struct ps_merge {
     int32_t seq;
     int32_t kv_head;
     int32_t row_begin;
     int32_t row_end;
-    int32_t partial_row; // split i's rows start at partial_row + i * (row_end - row_begin)
+    int32_t partial_row; // split i's row r is partial_row + i * split_stride + (r - row_begin)
     int32_t num_splits;
-    int32_t pad0, pad1;
+    int32_t split_stride; // rows of each split's partial block
+    int32_t pad;
 };
+// rows one merge workgroup covers: 256 threads, each 4 elements of a row
+inline int ps_merge_rows(int head_dim) { return 1024 / head_dim; }
 static_assert(sizeof(ps_merge) == 32, "ps_merge layout");
 
 // Tile geometry the planner and kernels agree on.

@@ -847,47 +847,36 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
 }
 
 // ---------------------------------------------------------------------------
-// Split-K merge: out = sum_i acc_i 2^(m_i - M) / sum_i l_i 2^(m_i - M).
+// Split-K merge: out = sum_i acc_i 2^(m_i - M) / sum_i l_i 2^(m_i - M),
+// M = max_i m_i. One workgroup per chunk of rows of one split set; each
+// thread owns 4 consecutive elements of one row.
 
 template <class DT, int D>
 __global__ __launch_bounds__(256) void ps_merge_kernel(const ps_attn_launch a) {
     using T = typename DT::T;
-    constexpr int CH = 8;
     const ps_merge mg = a.merges[blockIdx.x];
-    const int rows = mg.row_end - mg.row_begin;
+    const int row = threadIdx.x / (D / 4), d0 = (threadIdx.x % (D / 4)) * 4;
+    const int r = mg.row_begin + row;
+    if (r >= mg.row_end) return;
     const int g = a.num_q_heads / a.num_kv_heads;
-    const int qs0 = a.query_start_loc[mg.seq];
-    for (int u = threadIdx.x; u < rows * (D / CH); u += 256) {
-        const int row = u / (D / CH), d0 = (u - row * (D / CH)) * CH;
-        float M = kNegInf;
-        for (int sp = 0; sp < mg.num_splits; ++sp)
-            M = fmaxf(M, a.ws_m[(int64_t)mg.partial_row + (int64_t)sp * rows + row]);
-        const float muse = M == kNegInf ? 0.f : M;
-        float L = 0.f, acc[CH];
-#pragma unroll
-        for (int e = 0; e < CH; ++e) acc[e] = 0.f;
-        for (int sp = 0; sp < mg.num_splits; ++sp) {
-            const int64_t pr = (int64_t)mg.partial_row + (int64_t)sp * rows + row;
-            const float f = fast_exp2(a.ws_m[pr] - muse);
-            L += a.ws_l[pr] * f;
-            const f32x4 *ap = reinterpret_cast<const f32x4 *>(a.ws_acc + pr * D + d0);
-#pragma unroll
-            for (int e = 0; e < CH / 4; ++e) {
-                const f32x4 x = ap[e];
-                acc[4 * e + 0] += x[0] * f;
-                acc[4 * e + 1] += x[1] * f;
-                acc[4 * e + 2] += x[2] * f;
-                acc[4 * e + 3] += x[3] * f;
-            }
-        }
-        const int r = mg.row_begin + row;
-        const int tok = r / g;
-        const int h = mg.kv_head * g + (r - tok * g);
-        T *op = static_cast<T *>(a.out) + ((int64_t)(qs0 + tok) * a.num_q_heads + h) * D + d0;
-        const float inv = 1.f / L;
-#pragma unroll
-        for (int e = 0; e < CH; ++e) op[e] = cvt_out(acc[e] * inv, DT{});
+    const int64_t p0 = (int64_t)mg.partial_row + row;
+    float M = kNegInf;
+    for (int sp = 0; sp < mg.num_splits; ++sp) M = fmaxf(M, a.ws_m[p0 + (int64_t)sp * mg.split_stride]);
+    const float muse = M == kNegInf ? 0.f : M;
+    float L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < mg.num_splits; ++sp) {
+        const int64_t pr = p0 + (int64_t)sp * mg.split_stride;
+        const float f = fast_exp2(a.ws_m[pr] - muse);
+        L += a.ws_l[pr] * f;
+        acc += *reinterpret_cast<const f32x4 *>(a.ws_acc + pr * D + d0) * f;
     }
+    const int tok = r / g;
+    const int h = mg.kv_head * g + (r - tok * g);
+    T *op = static_cast<T *>(a.out) + ((int64_t)(a.query_start_loc[mg.seq] + tok) * a.num_q_heads + h) * D + d0;
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) op[e] = cvt_out(acc[e] * inv, DT{});
 }
 
 // ---------------------------------------------------------------------------

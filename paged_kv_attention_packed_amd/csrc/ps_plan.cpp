@@ -186,7 +186,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         }
         const int64_t dec_split = env_int(
             "PS_DECODE_SPLIT",
-            std::min<int64_t>(8192, std::max<int64_t>(128, round_up(ceil_div(dec_keys, 2048), 128))));
+            std::min<int64_t>(8192, std::max<int64_t>(128, round_up(ceil_div(dec_keys, 1024), 128))));
         const int64_t pre_split = env_int(
             "PS_PREFILL_SPLIT",
             // only long key ranges are worth splitting: the partials of a
@@ -222,14 +222,18 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                         (d ? dec : pre).push_back(it);
                     }
                     if (ns > 1) {
-                        ps_merge m{};
-                        m.seq = s;
-                        m.kv_head = j;
-                        m.row_begin = (int32_t)r0;
-                        m.row_end = (int32_t)r1;
-                        m.partial_row = (int32_t)base;
-                        m.num_splits = (int32_t)ns;
-                        mrg.push_back(m);
+                        const int64_t mr = ps_merge_rows(D);
+                        for (int64_t q0 = r0; q0 < r1; q0 += mr) {
+                            ps_merge m{};
+                            m.seq = s;
+                            m.kv_head = j;
+                            m.row_begin = (int32_t)q0;
+                            m.row_end = (int32_t)std::min(r1, q0 + mr);
+                            m.partial_row = (int32_t)(base + (q0 - r0));
+                            m.num_splits = (int32_t)ns;
+                            m.split_stride = (int32_t)(r1 - r0);
+                            mrg.push_back(m);
+                        }
                         ws_rows += ns * (r1 - r0);
                     }
                 }
