@@ -53,8 +53,21 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="measured FETCH/WRITE bytes per launch (from rocprofv3 --pmc), if present")
+                    help="measured FETCH/WRITE bytes per attention launch (from rocprofv3 --pmc)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (3 times): the "
+                         "reference kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_attention_packed_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def fill_context(P, step, pool, dev, stream):
@@ -224,12 +237,15 @@ def main():
     # plus q read, out write and block-table reads
     attn_bytes = info["kv_bytes_unique"] + info["q_bytes"] + info["out_bytes"] + info["table_bytes"]
     achieved = attn_bytes / (ms_attn * 1e-3) / 1e9
+    # measured HBM bytes per attention launch, valid only for the kernel
+    # sources the counters were taken with
     traffic = None
     if os.path.exists(args.traffic):
         try:
             with open(args.traffic) as f:
                 tr = json.load(f).get(step.name)
-            traffic = tr["bytes_per_launch"] if tr else None
+            if tr and tr.get("kernel_source_digest") == kernel_source_digest():
+                traffic = tr["bytes_per_launch"]
         except (OSError, ValueError, KeyError):
             traffic = None
     flops = info["flops_decode"] + info["flops_prefill"]
@@ -274,6 +290,14 @@ def main():
                                           capture_output=True, text=True, timeout=5).stdout.strip() or None
     except Exception:
         result["commit"] = None
+    if args.copy_mb > 0:
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    result["kernel_source_digest"] = kernel_source_digest()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline ...")
         result["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)

@@ -171,8 +171,10 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
             is_dec[s] = (flags == PS_PLAN_ALL_DECODE) ||
                         (flags == PS_PLAN_DEFAULT && rows <= PS_DEC_MAX_ROWS);
         }
-        // decode: a work item covers <= 32 packed rows and a slice of keys;
-        // slices are sized so the whole step yields a few thousand items
+        // decode: a work item covers <= 32 packed rows and a slice of keys.
+        // Slices are long (>= 2048 keys): a split costs a merge launch and
+        // partial traffic, which only pays off against long contexts; very
+        // long steps are cut into about 512 items (two per CU).
         int64_t dec_keys = 0, pre_keys = 0, pre_tiles = 0;
         for (int32_t s = 0; s < S; ++s) {
             const int64_t rows = (int64_t)g * q_lens[s], c = num_computed_tokens[s];
@@ -186,7 +188,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         }
         const int64_t dec_split = env_int(
             "PS_DECODE_SPLIT",
-            std::min<int64_t>(8192, std::max<int64_t>(128, round_up(ceil_div(dec_keys, 1024), 128))));
+            std::min<int64_t>(16384, std::max<int64_t>(2048, round_up(ceil_div(dec_keys, 512), 128))));
         const int64_t pre_split = env_int(
             "PS_PREFILL_SPLIT",
             // only long key ranges are worth splitting: the partials of a

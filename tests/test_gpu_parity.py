@@ -8,6 +8,8 @@ ps_paged_attention on cuda:0, then checks
     tolerance for the dtype: max-abs <= 1e-5 (fp32), 2e-3 (fp16),
     1e-2 (bf16), plus a per-row relative L2 bound.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -212,3 +214,18 @@ def test_empty_step_is_a_noop():
     step.run(q, k, k, pool, q, 0.1)
     torch.cuda.synchronize()
     assert torch.count_nonzero(pool_k) == 0
+
+
+@pytest.mark.parametrize("split", [16, 64, 2048])
+def test_forced_splits_merge_exactly(split, monkeypatch):
+    # short key slices force the split-K path (partials + merge kernel) on
+    # small steps, for both kernels
+    monkeypatch.setenv("PS_DECODE_SPLIT", str(split))
+    monkeypatch.setenv("PS_PREFILL_SPLIT", str(split))
+    for flags in (P.PS_PLAN_DEFAULT, P.PS_PLAN_ALL_DECODE, P.PS_PLAN_ALL_PREFILL):
+        for dt, hq, hkv, d in (("bf16", 12, 2, 128), ("f16", 14, 2, 64), ("f32", 4, 2, 64)):
+            st = workloads.random_step(300 + split + hq, dtype=dt, num_q_heads=hq, num_kv_heads=hkv,
+                                       head_dim=d, num_seqs=6, max_q=90, max_ctx=700)
+            _note(f"split={split} flags={flags} {dt} q_lens={st.q_lens.tolist()}")
+            out, _, _ = run_on_gpu(st, flags=flags)
+            check_out(st, out)

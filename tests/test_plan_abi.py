@@ -133,7 +133,7 @@ def test_validation_errors():
 
 
 def test_attention_argument_errors_return_before_any_launch():
-    st = workloads.config(2, values=False)
+    st = workloads.config(5, values=False)
     plan = _plan(st)
     pool = _pool(st)
     meta, ws = P.ps_plan_sizes(plan)
@@ -159,7 +159,7 @@ def test_attention_argument_errors_return_before_any_launch():
     # everything consistent, but the plan was never uploaded
     _expect_error(INV, call, match="uploaded")
     bad = _pool(st)
-    bad.head_dim = 128
+    bad.head_dim = 64
     _expect_error(INV, call, pool=bad, match="geometry")
 
 
