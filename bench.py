@@ -17,6 +17,10 @@ The pool is replicated so that consecutive timed steps touch different
 copies and the working set exceeds the 256 MB Infinity Cache plus L2:
 every step reads its K/V from HBM, as a real step would.
 
+Steps are timed replaying HIP graphs that captured them (the library's
+calls are plain kernel launches on the caller's stream, so a step can be
+captured); ``--eager`` times individual launches instead.
+
 Prints one JSON line on stdout; details go to stderr.
 """
 from __future__ import annotations
@@ -54,6 +58,9 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured FETCH/WRITE bytes per attention launch (from rocprofv3 --pmc)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time steps as individual launches instead of replaying them from a "
+                         "captured HIP graph")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times): the "
                          "reference kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
@@ -204,11 +211,37 @@ def main():
         one_step(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        one_step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    if args.eager:
+        e0.record(stream)
+        for i in range(args.steps):
+            one_step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    else:
+        # the steps, one per pool copy, captured once into HIP graphs: a
+        # block of nrot steps and a tail, replayed to give exactly K steps
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cs = torch.cuda.current_stream()
+                for i in range(n):
+                    ps.run(q, k, v, pools[i % nrot], outs[i % len(outs)], step.scale, cs)
+            return g
+        block = min(nrot, args.steps)
+        g_block = capture(block)
+        tail = args.steps % block
+        g_tail = capture(tail) if tail else None
+        for _ in range(2):  # replay warmup
+            g_block.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0.record(stream)
+        for _ in range(args.steps // block):
+            g_block.replay()
+        if g_tail is not None:
+            g_tail.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
     # ---- attention call alone (the dominant kernel(s)), same rotation
@@ -281,6 +314,7 @@ def main():
         "scatter_us": round(ms_scatter * 1e3, 3),
         "host_plan_us": round(host_plan_us, 1),
         "pool_copies": nrot,
+        "launch": "eager" if args.eager else "hip-graph replay",
         "gpu": torch.cuda.get_device_name(0),
         "torch": torch.__version__,
         "hip": torch.version.hip,

@@ -41,7 +41,6 @@ static_assert(sizeof(ps_merge) == 32, "ps_merge layout");
 // Tile geometry the planner and kernels agree on.
 constexpr int PS_BLOCK = 16;            // tokens per pool block
 constexpr int PS_DEC_TILE = 32;         // keys per decode-kernel wave iteration
-constexpr int PS_DEC_WAVES = 4;         // waves per decode work item
 constexpr int PS_DEC_MAX_ROWS = 32;     // packed rows per decode work item (two 16-row MFMA tiles)
 constexpr int PS_PRE_TILE = 64;         // keys per prefill LDS tile
 constexpr int PS_PRE_WAVES = 4;         // waves per prefill work item
@@ -92,6 +91,7 @@ struct ps_attn_launch {
     int32_t dtype;
     int32_t n_decode, n_prefill, n_merge;
     int32_t decode_row_tiles;
+    int32_t decode_waves;   // waves per decode workgroup (4, 8 or 16)
     float scale_log2;       // softmax scale * log2(e)
 };
 

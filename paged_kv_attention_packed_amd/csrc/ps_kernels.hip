@@ -275,16 +275,19 @@ __global__ __launch_bounds__(256) void ps_scatter_kernel(const u32x4 *__restrict
 // the slice round-robin, each double-buffering the next tile's K/V in
 // registers, then merge their softmax states through LDS.
 
-template <class DT, int D, int RT>
-__global__ __launch_bounds__(256, 2) void ps_decode_kernel(const ps_attn_launch a) {
+// NW waves per workgroup: more waves cover a short key slice in one round
+// trip (each wave takes every NW-th 32-key tile); the register budget
+// allows 2 waves per SIMD up to 8 waves and 4 per SIMD at 16.
+template <class DT, int D, int RT, int NW>
+__global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(const ps_attn_launch a) {
     using G = Geo<DT, D>;
     using T = typename DT::T;
     constexpr int ELT = G::ELT, KU4 = G::KU4, VW = G::VW, NT = G::NT, EPL = G::EPL;
     constexpr int ROWS = RT * 16;
 
-    __shared__ float sm_o[PS_DEC_WAVES][ROWS][D];
-    __shared__ float sm_m[PS_DEC_WAVES][ROWS];
-    __shared__ float sm_l[PS_DEC_WAVES][ROWS];
+    __shared__ float sm_o[NW][ROWS][D];
+    __shared__ float sm_m[NW][ROWS];
+    __shared__ float sm_l[NW][ROWS];
 
     const ps_item it = a.decode_items[blockIdx.x];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void ps_decode_kernel(const ps_attn_launch 
     if constexpr (!DOUBLE_BUFFER) {
         // two row tiles leave no registers for a second tile in flight;
         // the other resident waves cover the load latency
-        for (; ti < ntiles; ti += PS_DEC_WAVES) {
+        for (; ti < ntiles; ti += NW) {
             load_tile(B0{}, kb + ti * PS_DEC_TILE);
             compute_tile(B0{}, kb + ti * PS_DEC_TILE);
         }
@@ -414,13 +417,13 @@ __global__ __launch_bounds__(256, 2) void ps_decode_kernel(const ps_attn_launch 
     if constexpr (DOUBLE_BUFFER) {
         if (ti < ntiles) load_tile(B0{}, kb + ti * PS_DEC_TILE);
         while (ti < ntiles) {
-            if (ti + PS_DEC_WAVES < ntiles) load_tile(B1{}, kb + (ti + PS_DEC_WAVES) * PS_DEC_TILE);
+            if (ti + NW < ntiles) load_tile(B1{}, kb + (ti + NW) * PS_DEC_TILE);
             compute_tile(B0{}, kb + ti * PS_DEC_TILE);
-            ti += PS_DEC_WAVES;
+            ti += NW;
             if (ti >= ntiles) break;
-            if (ti + PS_DEC_WAVES < ntiles) load_tile(B0{}, kb + (ti + PS_DEC_WAVES) * PS_DEC_TILE);
+            if (ti + NW < ntiles) load_tile(B0{}, kb + (ti + NW) * PS_DEC_TILE);
             compute_tile(B1{}, kb + ti * PS_DEC_TILE);
-            ti += PS_DEC_WAVES;
+            ti += NW;
         }
     }
 
@@ -439,14 +442,15 @@ __global__ __launch_bounds__(256, 2) void ps_decode_kernel(const ps_attn_launch 
     }
     __syncthreads();
 
-    constexpr int EPT = ROWS * D / 256;  // output elements per thread
+    constexpr int EPT = ROWS * D / (64 * NW);  // output elements per thread (>= 1)
+    static_assert(EPT >= 1, "too many waves for the rows");
     const int e0 = tid * EPT;
     const int row = e0 / D, d0 = e0 % D;
     const int r = it.row_begin + row;
     if (r >= it.row_end) return;
-    float mw[PS_DEC_WAVES], M = kNegInf;
+    float mw[NW], M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < PS_DEC_WAVES; ++w) {
+    for (int w = 0; w < NW; ++w) {
         mw[w] = sm_m[w][row];
         M = fmaxf(M, mw[w]);
     }
@@ -455,7 +459,7 @@ __global__ __launch_bounds__(256, 2) void ps_decode_kernel(const ps_attn_launch 
 #pragma unroll
     for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int w = 0; w < PS_DEC_WAVES; ++w) {
+    for (int w = 0; w < NW; ++w) {
         const float f = fast_exp2(mw[w] - muse);
         L += sm_l[w][row] * f;
 #pragma unroll
@@ -897,10 +901,16 @@ int prefill_variant() {
 template <class DT, int D>
 hipError_t launch_attention_t(const ps_attn_launch &a, hipStream_t st) {
     if (a.n_decode > 0) {
-        if (a.decode_row_tiles == 1)
-            hipLaunchKernelGGL((ps_decode_kernel<DT, D, 1>), dim3(a.n_decode), dim3(256), 0, st, a);
-        else
-            hipLaunchKernelGGL((ps_decode_kernel<DT, D, 2>), dim3(a.n_decode), dim3(256), 0, st, a);
+        if (a.decode_row_tiles == 2) {
+            hipLaunchKernelGGL((ps_decode_kernel<DT, D, 2, 4>), dim3(a.n_decode), dim3(256), 0, st, a);
+        } else if (a.decode_waves >= 16 && D == 64 && DT::ELT == 2) {
+            if constexpr (D == 64 && DT::ELT == 2)  // 16 waves fit the register budget only here
+                hipLaunchKernelGGL((ps_decode_kernel<DT, D, 1, 16>), dim3(a.n_decode), dim3(1024), 0, st, a);
+        } else if (a.decode_waves >= 8) {
+            hipLaunchKernelGGL((ps_decode_kernel<DT, D, 1, 8>), dim3(a.n_decode), dim3(512), 0, st, a);
+        } else {
+            hipLaunchKernelGGL((ps_decode_kernel<DT, D, 1, 4>), dim3(a.n_decode), dim3(256), 0, st, a);
+        }
     }
     if (a.n_prefill > 0) {
         constexpr int TK = DT::ELT == 2 ? PS_PRE_TILE : PS_PRE_TILE / 2;

@@ -451,6 +451,10 @@ extern "C" ps_status ps_paged_attention(const void *q, const ps_pool *pool,
     a.n_prefill = plan->n_pre;
     a.n_merge = plan->n_mrg;
     a.decode_row_tiles = plan->dec_rt;
+    // few decode items: more waves per item, so a short slice is read in
+    // one round trip; many items: 4 waves each fill the chip
+    a.decode_waves = (int32_t)env_int("PS_DECODE_WAVES",
+                                      plan->n_dec < 512 ? (plan->D == 64 ? 16 : 8) : 4);
     a.scale_log2 = scale * 1.4426950408889634f;
     const int err = ps_launch_attention(a, stream);
     if (err != 0) return ps_fail(PS_ERR_HIP, "attention launch: %s", ps_hip_error_string(err));
