@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="time steps as individual launches instead of replaying them from a "
                          "captured HIP graph")
+    ap.add_argument("--op", default="step", choices=["step", "copy-blocks", "swap-blocks"],
+                    help="step: the packed step (default); copy-blocks: copy-on-write block copies "
+                         "in one device pool; swap-blocks: blocks out to a pinned host pool and back")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times): the "
                          "reference kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
@@ -146,12 +149,83 @@ def cpu_baseline(step, seconds):
             "sample": f"{reps} full steps of {step.name} (scatter + attention, fp64) in {el:.1f} s"}
 
 
+def bench_blocks(args):
+    """ps_copy_blocks throughput: copy-on-write inside the device pool, or
+    swap out to / in from a pinned host pool, on the chosen workload's pool."""
+    import numpy as np
+    import torch
+    import paged_kv_attention_packed_amd as P
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    step = workloads.config(args.config, values=False)
+    shape = (step.num_layers, step.num_blocks, 16, step.num_kv_heads, step.head_dim)
+    pk = torch.randn(shape, device=dev).to(step.dtype)
+    pv = torch.randn(shape, device=dev).to(step.dtype)
+    pool = P.make_pool(pk, pv)
+    rng = np.random.default_rng(args.config)
+    npairs = min(4096, step.num_blocks // 2)
+    perm = rng.permutation(step.num_blocks).astype(np.int32)
+    block_bytes = 16 * step.num_kv_heads * step.head_dim * pk.element_size() * step.num_layers
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e-3
+
+    if args.op == "copy-blocks":
+        src = torch.from_numpy(perm[:npairs]).to(dev)
+        dst = torch.from_numpy(perm[npairs:2 * npairs]).to(dev)
+        t = timed(lambda: P.ps_copy_blocks(pool, pool, src, dst, npairs, stream), args.steps)
+        moved = 2 * 2 * npairs * block_bytes  # K and V, read and written
+        result = {"metric": "copy-on-write block copy HBM GB/s, 1 MI355X", "value": round(moved / t / 1e9, 1),
+                  "unit": "GB/s", "us_per_launch": round(t * 1e6, 2),
+                  "roofline": {"bound": "hbm", "achieved": round(moved / t / 1e9, 1), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
+                               "traffic": None}}
+    else:
+        hshape = (step.num_layers, npairs, 16, step.num_kv_heads, step.head_dim)
+        hk = torch.empty(hshape, dtype=step.dtype, pin_memory=True)
+        hv = torch.empty(hshape, dtype=step.dtype, pin_memory=True)
+        host = P.make_pool(hk, hv)
+        blocks = torch.from_numpy(perm[:npairs]).to(dev)
+        slots = torch.arange(npairs, dtype=torch.int32, device=dev)
+        t_out = timed(lambda: P.ps_copy_blocks(pool, host, blocks, slots, npairs, stream), args.steps)
+        t_in = timed(lambda: P.ps_copy_blocks(host, pool, slots, blocks, npairs, stream), args.steps)
+        one_way = 2 * npairs * block_bytes
+        # the runtime's own copy of the same bytes, contiguous, for reference
+        flat_d = torch.empty(one_way, dtype=torch.uint8, device=dev)
+        flat_h = torch.empty(one_way, dtype=torch.uint8, pin_memory=True)
+        t_ref = timed(lambda: flat_h.copy_(flat_d, non_blocking=True), args.steps)
+        result = {"metric": "swap out / in block copy GB/s over the host link, 1 MI355X",
+                  "value": round(one_way / t_out / 1e9, 2), "unit": "GB/s (swap out)",
+                  "swap_in_gbs": round(one_way / t_in / 1e9, 2),
+                  "contiguous_d2h_memcpy_gbs": round(one_way / t_ref / 1e9, 2),
+                  "us_per_launch": {"out": round(t_out * 1e6, 1), "in": round(t_in * 1e6, 1)}}
+    result.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                   "dtype": step.dtype_name, "data": "synthetic",
+                   "config": {"workload": step.name, "op": args.op, "pairs": npairs,
+                              "block_bytes_all_layers_kv": 2 * block_bytes}})
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
+    if args.op != "step":
+        bench_blocks(args)
+        return
     import numpy as np
     import torch
     import paged_kv_attention_packed_amd as P

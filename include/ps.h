@@ -223,6 +223,29 @@ ps_status ps_paged_attention(const void *q, const ps_pool *pool,
                              float scale, const ps_plan *plan,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Copy whole blocks between two pools of the same layout (num_layers,
+ * block_size, num_kv_heads, head_dim, dtype; num_blocks may differ): for
+ * every pair i and every layer, block src_blocks[i] of (src->k, src->v) is
+ * copied byte for byte to block dst_blocks[i] of (dst->k, dst->v). The
+ * `layer` fields are ignored: a block id names storage in every layer
+ * (PageServe, "06 Development history", phase 7).
+ *
+ * This is the data movement of copy-on-write (same pool: a shared block
+ * is duplicated before a sequence writes into it; tinyserve README, "How
+ * it works") and of swapping a preempted sequence's blocks out to a pinned
+ * host pool and back in (PageServe, "04 Preemption"; tinyserve README,
+ * "How it works"). Host pools must be pinned, device-accessible memory
+ * (hipHostMalloc, torch pin_memory).
+ *
+ *   src_blocks, dst_blocks  device (or device-accessible) [num_pairs]; a
+ *                           pair with an id outside its pool is skipped.
+ *                           Destination ids must be distinct and must not
+ *                           be read by another pair of the same call.
+ */
+ps_status ps_copy_blocks(const ps_pool *src, const ps_pool *dst, const int32_t *src_blocks,
+                         const int32_t *dst_blocks, int32_t num_pairs, void *stream);
+
 const char *ps_status_string(ps_status status);
 
 /* Reason for the calling thread's last failed call ("" if none). */

@@ -62,6 +62,9 @@ def _load():
         _f64p, _f64p, _f64p, _f64p, _f64p, _i32p, _i32p, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
         _u8p, _f64p]
+    lib.oracle_copy_blocks.restype = None
+    lib.oracle_copy_blocks.argtypes = [_u8p, _u8p, _u8p, _u8p, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int64, _i32p, _i32p, ctypes.c_int32]
     lib.oracle_num_threads.restype = ctypes.c_int32
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -185,3 +188,16 @@ def kv_bytes_per_block(num_layers: int, block_size: int, num_kv_heads: int,
     """K+V bytes one block holds across all layers (tinyserve README,
     "Memory accounting": 2 x layers x block_size x kv heads x head_dim x dtype)."""
     return 2 * num_layers * block_size * num_kv_heads * head_dim * elt_bytes
+
+
+def copy_blocks(src_k, src_v, dst_k, dst_v, src_ids, dst_ids):
+    """Copy whole blocks (every layer, K and V) between pools of one layout."""
+    L, NBs, bs, hkv, d, elt = _pool_geometry(src_k)
+    L2, NBd, bs2, hkv2, d2, elt2 = _pool_geometry(dst_k)
+    assert (L, bs, hkv, d, elt) == (L2, bs2, hkv2, d2, elt2)
+    si, di = _i32(src_ids), _i32(dst_ids)
+    assert si.shape == di.shape
+    _load().oracle_copy_blocks(
+        src_k.view(np.uint8).ctypes.data_as(_u8p), src_v.view(np.uint8).ctypes.data_as(_u8p),
+        dst_k.view(np.uint8).ctypes.data_as(_u8p), dst_v.view(np.uint8).ctypes.data_as(_u8p),
+        L, NBs, NBd, bs * hkv * d * elt, _ptr(si, ctypes.c_int32), _ptr(di, ctypes.c_int32), len(si))

@@ -214,6 +214,28 @@ void oracle_attention(const double *q, const double *kctx, const double *vctx,
     free(seq_c0);
 }
 
+/*
+ * Block copy: for each pair and each layer, block src_ids[i] of the source
+ * pools is copied to block dst_ids[i] of the destination pools, K and V
+ * (copy-on-write and swap move whole blocks; PageServe "04 Preemption",
+ * tinyserve README "How it works"). block_bytes is one layer's block of one
+ * pool: block_size * Hkv * D * elt.
+ */
+void oracle_copy_blocks(const uint8_t *src_k, const uint8_t *src_v, uint8_t *dst_k, uint8_t *dst_v,
+                        int32_t num_layers, int32_t src_blocks, int32_t dst_blocks,
+                        int64_t block_bytes, const int32_t *src_ids, const int32_t *dst_ids,
+                        int32_t num_pairs)
+{
+    for (int32_t i = 0; i < num_pairs; ++i) {
+        for (int32_t l = 0; l < num_layers; ++l) {
+            const int64_t so = ((int64_t)l * src_blocks + src_ids[i]) * block_bytes;
+            const int64_t d0 = ((int64_t)l * dst_blocks + dst_ids[i]) * block_bytes;
+            memcpy(dst_k + d0, src_k + so, (size_t)block_bytes);
+            memcpy(dst_v + d0, src_v + so, (size_t)block_bytes);
+        }
+    }
+}
+
 /* Threads the OpenMP runtime will use for oracle_attention. */
 int32_t oracle_num_threads(void)
 {

@@ -32,7 +32,8 @@ PS_PLAN_DEFAULT, PS_PLAN_ALL_DECODE, PS_PLAN_ALL_PREFILL = 0, 1, 2
 EXPORTED = [
     "ps_plan_step", "ps_plan_sizes", "ps_plan_upload", "ps_plan_device_arrays",
     "ps_plan_host_arrays", "ps_plan_get_info", "ps_plan_destroy", "ps_reshape_and_cache",
-    "ps_paged_attention", "ps_status_string", "ps_last_error_message", "ps_abi_version",
+    "ps_paged_attention", "ps_copy_blocks", "ps_status_string", "ps_last_error_message",
+    "ps_abi_version",
 ]
 
 
@@ -98,6 +99,8 @@ lib.ps_paged_attention.restype = ctypes.c_int32
 lib.ps_paged_attention.argtypes = [_vp, ctypes.POINTER(ps_pool), _vp, ctypes.c_int32, _vp, _vp, _vp,
                                    _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_float, _vp, _vp, _sz, _vp]
+lib.ps_copy_blocks.restype = ctypes.c_int32
+lib.ps_copy_blocks.argtypes = [ctypes.POINTER(ps_pool), ctypes.POINTER(ps_pool), _vp, _vp, ctypes.c_int32, _vp]
 lib.ps_status_string.restype = ctypes.c_char_p
 lib.ps_status_string.argtypes = [ctypes.c_int32]
 lib.ps_last_error_message.restype = ctypes.c_char_p
@@ -226,6 +229,11 @@ def ps_paged_attention(q, pool: ps_pool, block_tables, block_table_stride: int, 
                                   _ptr(query_start_loc), _ptr(num_computed_tokens), _ptr(context_lens),
                                   _ptr(out), num_seqs, num_tokens, num_q_heads, scale, plan.handle,
                                   _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def ps_copy_blocks(src: ps_pool, dst: ps_pool, src_blocks, dst_blocks, num_pairs: int, stream=None):
+    _check(lib.ps_copy_blocks(ctypes.byref(src), ctypes.byref(dst), _ptr(src_blocks), _ptr(dst_blocks),
+                              num_pairs, _stream(stream)))
 
 
 def ps_abi_version() -> int:

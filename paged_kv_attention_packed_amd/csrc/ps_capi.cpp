@@ -56,3 +56,35 @@ extern "C" ps_status ps_reshape_and_cache(const void *k, const void *v, const in
     if (err != 0) return ps_fail(PS_ERR_HIP, "scatter launch: %s", ps_hip_error_string(err));
     return PS_OK;
 }
+
+static ps_status check_pool_layout(const ps_pool *p, const char *what) {
+    if (!p) return ps_fail(PS_ERR_INVALID_ARGUMENT, "%s pool is NULL", what);
+    if (p->block_size != PS_BLOCK)
+        return ps_fail(PS_ERR_UNSUPPORTED, "%s pool: block_size %d (only 16 is supported)", what, p->block_size);
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return ps_fail(PS_ERR_UNSUPPORTED, "%s pool: head_dim %d (64 or 128 supported)", what, p->head_dim);
+    if (p->dtype != PS_F32 && p->dtype != PS_F16 && p->dtype != PS_BF16)
+        return ps_fail(PS_ERR_UNSUPPORTED, "%s pool: dtype %d", what, p->dtype);
+    if (p->num_kv_heads < 1 || p->num_layers < 1 || p->num_blocks < 1)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "%s pool needs num_kv_heads, num_layers, num_blocks >= 1", what);
+    return PS_OK;
+}
+
+extern "C" ps_status ps_copy_blocks(const ps_pool *src, const ps_pool *dst, const int32_t *src_blocks,
+                                    const int32_t *dst_blocks, int32_t num_pairs, void *stream) {
+    ps_status st = check_pool_layout(src, "source");
+    if (st != PS_OK) return st;
+    if ((st = check_pool_layout(dst, "destination")) != PS_OK) return st;
+    if (src->num_layers != dst->num_layers || src->num_kv_heads != dst->num_kv_heads ||
+        src->head_dim != dst->head_dim || src->dtype != dst->dtype)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "source and destination pools differ in layout");
+    if (num_pairs < 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_pairs < 0");
+    if (num_pairs == 0) return PS_OK;
+    if (!src_blocks || !dst_blocks || !src->k || !src->v || !dst->k || !dst->v)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "a device pointer is NULL");
+    if ((int64_t)num_pairs * src->num_layers > 0x7fffffff)
+        return ps_fail(PS_ERR_UNSUPPORTED, "too many block copies in one call");
+    const int err = ps_launch_copy_blocks(src, dst, src_blocks, dst_blocks, num_pairs, stream);
+    if (err != 0) return ps_fail(PS_ERR_HIP, "copy launch: %s", ps_hip_error_string(err));
+    return PS_OK;
+}

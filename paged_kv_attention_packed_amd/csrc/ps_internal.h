@@ -99,6 +99,8 @@ struct ps_attn_launch {
 int ps_launch_scatter(const void *k, const void *v, const int32_t *slot_mapping,
                       int32_t num_tokens, const ps_pool *pool, void *stream);
 int ps_launch_attention(const ps_attn_launch &a, void *stream);
+int ps_launch_copy_blocks(const ps_pool *src, const ps_pool *dst, const int32_t *src_blocks,
+                          const int32_t *dst_blocks, int32_t num_pairs, void *stream);
 const char *ps_hip_error_string(int err);
 
 // Set the calling thread's error message (ps_capi.cpp).

@@ -270,6 +270,31 @@ __global__ __launch_bounds__(256) void ps_scatter_kernel(const u32x4 *__restrict
 }
 
 // ---------------------------------------------------------------------------
+// Block copy (copy-on-write, swap out / in): one workgroup per (pair,
+// layer) moves that layer's K and V block, 16 bytes per thread per step.
+
+__global__ __launch_bounds__(256) void ps_copy_blocks_kernel(const u32x4 *__restrict__ sk,
+                                                             const u32x4 *__restrict__ sv,
+                                                             u32x4 *__restrict__ dk, u32x4 *__restrict__ dv,
+                                                             const int32_t *__restrict__ src_ids,
+                                                             const int32_t *__restrict__ dst_ids,
+                                                             int32_t num_layers, int32_t src_blocks,
+                                                             int32_t dst_blocks, int32_t block_words) {
+    const int pair = blockIdx.x / num_layers;
+    const int layer = blockIdx.x - pair * num_layers;
+    const int32_t s = src_ids[pair], d = dst_ids[pair];
+    if ((uint32_t)s >= (uint32_t)src_blocks || (uint32_t)d >= (uint32_t)dst_blocks) return;
+    const int64_t so = ((int64_t)layer * src_blocks + s) * block_words;
+    const int64_t do_ = ((int64_t)layer * dst_blocks + d) * block_words;
+    for (int w = threadIdx.x; w < block_words; w += 256) {
+        const u32x4 a = sk[so + w];
+        const u32x4 b = sv[so + w];
+        dk[do_ + w] = a;
+        dv[do_ + w] = b;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Decode / verify attention. One workgroup = one work item (sequence, KV
 // head, <= RT*16 packed rows, key slice). Its 4 waves take 32-key tiles of
 // the slice round-robin, each double-buffering the next tile's K/V in
@@ -967,6 +992,18 @@ int ps_launch_scatter(const void *k, const void *v, const int32_t *slot_mapping,
                        static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(k),
                        static_cast<const u32x4 *>(v), slot_mapping, total, row_words, pk, pv,
                        pool->num_blocks * PS_BLOCK);
+    return (int)hipGetLastError();
+}
+
+int ps_launch_copy_blocks(const ps_pool *src, const ps_pool *dst, const int32_t *src_blocks,
+                          const int32_t *dst_blocks, int32_t num_pairs, void *stream) {
+    const int elt = src->dtype == PS_F32 ? 4 : 2;
+    const int32_t block_words = (int32_t)((int64_t)PS_BLOCK * src->num_kv_heads * src->head_dim * elt / 16);
+    hipLaunchKernelGGL(ps_copy_blocks_kernel, dim3((unsigned)(num_pairs * src->num_layers)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(src->k),
+                       static_cast<const u32x4 *>(src->v), static_cast<u32x4 *>(dst->k),
+                       static_cast<u32x4 *>(dst->v), src_blocks, dst_blocks, src->num_layers,
+                       src->num_blocks, dst->num_blocks, block_words);
     return (int)hipGetLastError();
 }
 

@@ -280,3 +280,52 @@ def test_config1_matches_full_matrix_form():
     t_first_chunk = 4
     for h in range(2):
         np.testing.assert_array_equal(out[t_first_chunk, h], H.f64(st.v)[t_first_chunk, 0])
+
+
+# --------------------------------------------------------------------------
+# block copy (copy-on-write, swap out / in)
+
+
+def _pools_with_context(seed, layers=2):
+    st = workloads.random_step(seed, dtype="bf16", num_q_heads=4, num_kv_heads=2, head_dim=64,
+                               num_seqs=4, max_q=8, max_ctx=60, num_layers=layers, layer=layers - 1)
+    return st, H.host_pools(st)
+
+
+def test_swap_round_trip_is_lossless():
+    # tinyserve README "Correctness & testing": swap round-trip losslessness
+    st, (pk, pv) = _pools_with_context(31)
+    used = np.unique(st.block_tables[st.block_tables >= 0])
+    host_k = np.zeros((pk.shape[0], len(used)) + pk.shape[2:], dtype=pk.dtype)
+    host_v = np.zeros_like(host_k)
+    oracle.copy_blocks(pk, pv, host_k, host_v, used, np.arange(len(used)))
+    back_k = np.full_like(pk, 7)
+    back_v = np.full_like(pv, 7)
+    oracle.copy_blocks(host_k, host_v, back_k, back_v, np.arange(len(used)), used)
+    np.testing.assert_array_equal(back_k[:, used], pk[:, used])
+    np.testing.assert_array_equal(back_v[:, used], pv[:, used])
+    rest = np.setdiff1d(np.arange(pk.shape[1]), used)
+    assert np.all(back_k[:, rest] == 7) and np.all(back_v[:, rest] == 7)
+
+
+def test_copy_on_write_duplicate_serves_the_same_tokens():
+    # tinyserve README "How it works": a write into a shared block first
+    # copies it; the copy must read back exactly as the original
+    st, (pk, pv) = _pools_with_context(32)
+    s = int(np.argmax(st.num_computed))
+    n = int(st.num_computed[s])
+    row = st.block_tables[s].copy()
+    free = np.setdiff1d(np.arange(pk.shape[1]), st.block_tables[st.block_tables >= 0])
+    last = (n - 1) // 16
+    before_k, before_v = pk.copy(), pv.copy()
+    oracle.copy_blocks(pk, pv, pk, pv, [row[last]], [free[0]])
+    new_row = row.copy()
+    new_row[last] = free[0]
+    for layer in range(pk.shape[0]):
+        a = oracle.gather(pk, pv, layer, row, n)
+        b = oracle.gather(pk, pv, layer, new_row, n)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+    # only the destination block changed
+    diff = np.any(pk != before_k, axis=(0, 2, 3, 4)) | np.any(pv != before_v, axis=(0, 2, 3, 4))
+    assert set(np.nonzero(diff)[0].tolist()) <= {int(free[0])}
