@@ -14,7 +14,8 @@ PageServe "01 Scheduler loop" (Pack / Execute, System architecture),
 "06 Development history" phase 7 (pool [layers, blocks, 16, H, D]) and
 phase 8 (one packed [1, T] pass); tinyserve README "How it works" (two
 K/V slabs, block tables, stepped causal mask for verify rows) and
-"Highlights" (grouped-query attention).
+"Highlights" (grouped-query attention, rotary embeddings of the Qwen2
+forward pass).
 """
 from __future__ import annotations
 
@@ -65,6 +66,9 @@ def _load():
     lib.oracle_copy_blocks.restype = None
     lib.oracle_copy_blocks.argtypes = [_u8p, _u8p, _u8p, _u8p, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int64, _i32p, _i32p, ctypes.c_int32]
+    lib.oracle_rope.restype = None
+    lib.oracle_rope.argtypes = [_f64p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _i32p,
+                                ctypes.c_double, _f64p]
     lib.oracle_num_threads.restype = ctypes.c_int32
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -201,3 +205,21 @@ def copy_blocks(src_k, src_v, dst_k, dst_v, src_ids, dst_ids):
         src_k.view(np.uint8).ctypes.data_as(_u8p), src_v.view(np.uint8).ctypes.data_as(_u8p),
         dst_k.view(np.uint8).ctypes.data_as(_u8p), dst_v.view(np.uint8).ctypes.data_as(_u8p),
         L, NBs, NBd, bs * hkv * d * elt, _ptr(si, ctypes.c_int32), _ptr(di, ctypes.c_int32), len(si))
+
+
+def rope(x, positions, theta: float):
+    """Rotary embedding of ``x`` [T, H, D] at per-row ``positions`` [T] (fp64).
+
+    Pair (x[j], x[j + D/2]) turns by positions[t] * theta^(-2j/D) (the
+    Qwen2 rotation; tinyserve README "Highlights").
+    """
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    assert x.ndim == 3 and x.shape[2] % 2 == 0
+    T, H, D = x.shape
+    pos = _i32(positions)
+    assert pos.shape == (T,)
+    out = np.empty_like(x)
+    if T:
+        _load().oracle_rope(_ptr(x, ctypes.c_double), T, H, D, _ptr(pos, ctypes.c_int32),
+                            float(theta), _ptr(out, ctypes.c_double))
+    return out

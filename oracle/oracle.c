@@ -31,6 +31,12 @@
  *    token at position p of sequence s, head h, attends keys 0..p of s
  *    through KV head h / (Hq / Hkv) with softmax(scale * q.k) weights.
  *
+ *  - rotary position embedding: tinyserve README, "Highlights" (the Qwen2
+ *    forward pass applies rotary embeddings) with PageServe "01 Scheduler
+ *    loop" (Pack: explicit position_ids). Read as Qwen2's rotation: for
+ *    j < D/2 the pair (x[j], x[j + D/2]) turns by the angle
+ *    pos * theta^(-2j/D).
+ *
  * Everything is fp64; inputs arrive already rounded to the storage dtype
  * and upcast by the caller.
  */
@@ -232,6 +238,34 @@ void oracle_copy_blocks(const uint8_t *src_k, const uint8_t *src_v, uint8_t *dst
             const int64_t d0 = ((int64_t)l * dst_blocks + dst_ids[i]) * block_bytes;
             memcpy(dst_k + d0, src_k + so, (size_t)block_bytes);
             memcpy(dst_v + d0, src_v + so, (size_t)block_bytes);
+        }
+    }
+}
+
+/*
+ * Rotary position embedding of T rows of H heads each ([T, H, D], fp64):
+ * row t is at position positions[t]. For each head and j in [0, D/2),
+ * with a = positions[t] * theta^(-2j/D):
+ *   out[j]       = x[j] cos a - x[j + D/2] sin a
+ *   out[j + D/2] = x[j + D/2] cos a + x[j] sin a
+ * i.e. the complex number x[j] + i x[j + D/2] multiplied by e^{ia}.
+ * out may equal x.
+ */
+void oracle_rope(const double *x, int64_t T, int32_t H, int32_t D, const int32_t *positions,
+                 double theta, double *out)
+{
+    const int32_t half = D / 2;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < half; ++j) {
+            const double a = (double)positions[t] * pow(theta, -2.0 * j / D);
+            const double c = cos(a), s = sin(a);
+            for (int32_t h = 0; h < H; ++h) {
+                const double *xr = x + (t * H + h) * D;
+                double *orow = out + (t * H + h) * D;
+                const double x1 = xr[j], x2 = xr[j + half];
+                orow[j] = x1 * c - x2 * s;
+                orow[j + half] = x2 * c + x1 * s;
+            }
         }
     }
 }

@@ -10,7 +10,11 @@ mathematics fix, independent of the oracle's own code.
  * invariances the pages state: chunked prefill equals full prefill,
    a 1 + k verify equals k + 1 successive decodes, physical block
    placement and prefix sharing do not change what a sequence reads;
- * a second formulation (full-matrix numpy) on tiny inputs.
+ * a second formulation (full-matrix numpy) on tiny inputs;
+ * rotary embedding: the transformers Qwen2 rotary routine at small
+   positions, the two-dimensional case (a plane rotation by the position),
+   pair-norm preservation, scores that depend on relative position only,
+   and additive composition of rotations.
 """
 import json
 import math
@@ -329,3 +333,84 @@ def test_copy_on_write_duplicate_serves_the_same_tokens():
     # only the destination block changed
     diff = np.any(pk != before_k, axis=(0, 2, 3, 4)) | np.any(pv != before_v, axis=(0, 2, 3, 4))
     assert set(np.nonzero(diff)[0].tolist()) <= {int(free[0])}
+
+
+# --------------------------------------------------------------------------
+# rotary position embedding (tinyserve README "Highlights": the Qwen2 forward
+# applies rotary embeddings; PageServe "01 Scheduler loop": explicit
+# position_ids per packed token)
+
+
+@pytest.mark.parametrize("d,theta", [(64, 1e4), (128, 1e6)])
+def test_rope_matches_transformers_qwen2(d, theta):
+    # library routine: the Qwen2 rotary embedding of the transformers
+    # package. It forms its angles and cos/sin in fp32, so positions stay
+    # small (< 64) and the tolerance covers fp32 angle rounding
+    # (64 * 2^-24 * |x| per element).
+    transformers = pytest.importorskip("transformers")
+    from transformers.models.qwen2.modeling_qwen2 import Qwen2RotaryEmbedding, apply_rotary_pos_emb
+    cfg = transformers.Qwen2Config(hidden_size=d * 4, num_attention_heads=4, num_key_value_heads=2,
+                                   rope_theta=theta)
+    rot = Qwen2RotaryEmbedding(config=cfg)
+    rng = np.random.default_rng(7)
+    T = 48
+    pos = rng.integers(0, 64, T)
+    x = rng.standard_normal((T, 3, d))
+    xt = torch.from_numpy(x).permute(1, 0, 2)[None]  # [1, H, T, D]
+    cos, sin = rot(xt, torch.from_numpy(pos)[None])
+    ref, _ = apply_rotary_pos_emb(xt, xt, cos, sin)
+    ref = ref[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(oracle.rope(x, pos, theta), ref, rtol=0, atol=5e-5)
+
+
+def test_rope_position_zero_is_identity():
+    x = np.random.default_rng(1).standard_normal((5, 4, 64))
+    assert np.array_equal(oracle.rope(x, np.zeros(5, np.int32), 1e6), x)
+
+
+def test_rope_two_dims_is_a_plane_rotation_by_the_position():
+    # D = 2: one pair, frequency theta^0 = 1, so the angle is the position
+    # itself: multiply x0 + i x1 by e^{i pos}
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((9, 1, 2))
+    pos = np.array([0, 1, 2, 3, 7, 100, 12345, 10**6, 2**30], np.int32)
+    z = (x[:, 0, 0] + 1j * x[:, 0, 1]) * np.exp(1j * pos.astype(np.float64))
+    got = oracle.rope(x, pos, 10.0)
+    np.testing.assert_allclose(got[:, 0, 0], z.real, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(got[:, 0, 1], z.imag, rtol=0, atol=1e-9)
+
+
+def test_rope_preserves_every_pair_norm():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((16, 3, 128))
+    pos = rng.integers(0, 1 << 20, 16)
+    y = oracle.rope(x, pos, 1e6)
+    h = 64
+    np.testing.assert_allclose(y[..., :h] ** 2 + y[..., h:] ** 2, x[..., :h] ** 2 + x[..., h:] ** 2,
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_rope_scores_depend_only_on_relative_position():
+    # <R(m) q, R(n) k> is a function of m - n alone
+    rng = np.random.default_rng(4)
+    for d, theta in [(64, 1e4), (128, 1e6)]:
+        q = rng.standard_normal((1, 1, d))
+        k = rng.standard_normal((1, 1, d))
+        for m, n, delta in [(5, 2, 11), (0, 0, 1000), (300, 17, 4096), (9, 40, 77777)]:
+            a = np.sum(oracle.rope(q, [m], theta) * oracle.rope(k, [n], theta))
+            b = np.sum(oracle.rope(q, [m + delta], theta) * oracle.rope(k, [n + delta], theta))
+            assert abs(a - b) <= 1e-9 * (1 + abs(a)), (d, m, n, delta)
+        # and the relative offset matters (the rotation is not trivial)
+        a = np.sum(oracle.rope(q, [3], theta) * oracle.rope(k, [0], theta))
+        b = np.sum(oracle.rope(q, [4], theta) * oracle.rope(k, [0], theta))
+        assert abs(a - b) > 1e-3
+
+
+def test_rope_rotations_compose_additively():
+    # turning by position a and then by position b equals turning by a + b
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((6, 2, 64))
+    a = np.array([0, 1, 31, 500, 4096, 70000], np.int32)
+    b = np.array([3, 0, 33, 12, 4095, 1], np.int32)
+    np.testing.assert_allclose(oracle.rope(oracle.rope(x, a, 1e4), b, 1e4), oracle.rope(x, a + b, 1e4),
+                               rtol=0, atol=1e-9)
