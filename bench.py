@@ -61,9 +61,10 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="time steps as individual launches instead of replaying them from a "
                          "captured HIP graph")
-    ap.add_argument("--op", default="step", choices=["step", "copy-blocks", "swap-blocks"],
+    ap.add_argument("--op", default="step", choices=["step", "copy-blocks", "swap-blocks", "rope-cache"],
                     help="step: the packed step (default); copy-blocks: copy-on-write block copies "
-                         "in one device pool; swap-blocks: blocks out to a pinned host pool and back")
+                         "in one device pool; swap-blocks: blocks out to a pinned host pool and back; "
+                         "rope-cache: rotary embedding of the step's q and k fused with the KV scatter")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times): the "
                          "reference kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
@@ -217,12 +218,79 @@ def bench_blocks(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_rope(args):
+    """ps_rope_reshape_and_cache throughput on the chosen workload's new tokens:
+    q rotated into q_out, k rotated into the pool, v copied into the pool.
+    Input sets and slot placements rotate so that the working set between
+    reuses exceeds the Infinity Cache."""
+    import numpy as np
+    import torch
+    import paged_kv_attention_packed_amd as P
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    step = workloads.config(args.config, values=False)
+    T, hq, hkv, d = step.num_tokens, step.num_q_heads, step.num_kv_heads, step.head_dim
+    shape = (step.num_layers, step.num_blocks, 16, hkv, d)
+    pk = torch.zeros(shape, dtype=step.dtype, device=dev)
+    pv = torch.zeros(shape, dtype=step.dtype, device=dev)
+    pool = P.make_pool(pk, pv, step.layer)
+    ps = P.PackedStep(step.q_lens, step.num_computed, step.block_tables, hq, pool, dev, stream=stream)
+    host = P.ps_plan_host_arrays(ps.plan, step.num_seqs, T)
+    elt = pk.element_size()
+    moved = T * (2 * hq * d * elt + 4 * hkv * d * elt + 8)   # q in/out, k and v in/out, position + slot
+    nrot = min(1024, max(1, math.ceil(ROTATE_TARGET / moved)))
+    rng = np.random.default_rng(args.config)
+    g = torch.Generator(device=dev).manual_seed(args.config)
+    sets = []
+    for r in range(nrot):
+        perm = rng.permutation(step.num_blocks).astype(np.int64)
+        sl = host["slot_mapping"].astype(np.int64)
+        slots = (perm[sl // 16] * 16 + sl % 16).astype(np.int32)
+        sets.append((torch.randn((T, hq, d), generator=g, device=dev).to(step.dtype),
+                     torch.empty((T, hq, d), dtype=step.dtype, device=dev),
+                     torch.randn((T, hkv, d), generator=g, device=dev).to(step.dtype),
+                     torch.randn((T, hkv, d), generator=g, device=dev).to(step.dtype),
+                     torch.from_numpy(host["positions"]).to(dev), torch.from_numpy(slots).to(dev)))
+    theta = 1e6
+
+    def launch(i):
+        q, qo, k, v, pos, sl = sets[i % nrot]
+        P.ps_rope_reshape_and_cache(q, qo, k, v, pos, sl, T, hq, theta, pool, stream)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        launch(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / args.steps * 1e-3
+    gbs = moved / t / 1e9
+    result = {"metric": "rotary embedding + KV scatter HBM GB/s, 1 MI355X", "value": round(gbs, 1),
+              "unit": "GB/s", "us_per_launch": round(t * 1e6, 2),
+              "tokens_per_s": round(T / t, 1),
+              "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+              "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+              "dtype": step.dtype_name, "data": "synthetic",
+              "config": {"workload": step.name, "op": args.op, "tokens": T, "rope_theta": theta,
+                         "bytes_per_launch": moved, "input_sets": nrot}}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
+    if args.op == "rope-cache":
+        bench_rope(args)
+        return
     if args.op != "step":
         bench_blocks(args)
         return

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define PS_ABI_VERSION 1
+#define PS_ABI_VERSION 2
 
 typedef int32_t ps_status;
 enum {
@@ -149,6 +149,7 @@ typedef struct {
     const int32_t *query_start_loc;     /* [S + 1] exclusive prefix sum of q_lens */
     const int32_t *num_computed_tokens; /* [S] */
     const int32_t *context_lens;        /* [S]   c_s + n_s */
+    const int32_t *positions;           /* [T]   position c_s + i of each packed token */
 } ps_step_arrays;
 
 ps_status ps_plan_device_arrays(const ps_plan *plan, ps_step_arrays *arrays);
@@ -245,6 +246,43 @@ ps_status ps_paged_attention(const void *q, const ps_pool *pool,
  */
 ps_status ps_copy_blocks(const ps_pool *src, const ps_pool *dst, const int32_t *src_blocks,
                          const int32_t *dst_blocks, int32_t num_pairs, void *stream);
+
+/*
+ * Rotary position embedding fused with the KV scatter: the step just
+ * upstream of attention in the packed forward pass (tinyserve README,
+ * "Highlights": the Qwen2 forward applies rotary embeddings to a
+ * flattened ragged batch; PageServe "01 Scheduler loop", Pack: explicit
+ * position_ids and a slot per token). For packed token t at position
+ * p = positions[t] and every head, each pair (x[j], x[j + D/2]),
+ * j < D/2, is turned by the angle p * rope_theta^(-2j/D):
+ *   y[j]       = x[j] cos a - x[j + D/2] sin a
+ *   y[j + D/2] = x[j + D/2] cos a + x[j] sin a
+ * (the Qwen2 pairing of a head's halves). Then
+ *   q_out[t, h, :]                         = rotated q[t, h, :]
+ *   pool.k[layer, slot/16, slot%16, j, :]  = rotated k[t, j, :]
+ *   pool.v[layer, slot/16, slot%16, j, :]  = v[t, j, :]   (byte copy)
+ * with slot = slot_mapping[t]. This replaces ps_reshape_and_cache for a
+ * step whose K arrives unrotated.
+ *
+ * Angles are formed in fp64 (an exact product of the position and a
+ * host-computed fp64 frequency), cos and sin in fp64, the rotation in fp32;
+ * results are rounded to the pool dtype (round to nearest even).
+ *
+ *   q, q_out      device [num_tokens, num_q_heads, head_dim], pool dtype.
+ *                 q_out may equal q (rotation in place); otherwise the two
+ *                 must not overlap. Both may be NULL when num_q_heads = 0
+ *                 (K rotation and scatter only).
+ *   k, v          device [num_tokens, num_kv_heads, head_dim], pool dtype
+ *   positions     device [num_tokens] int32 (e.g. ps_step_arrays.positions)
+ *   slot_mapping  device [num_tokens], distinct slots in [0, num_blocks*16);
+ *                 a token whose slot is outside that range writes nothing
+ *                 to the pool (its q is still rotated)
+ *   rope_theta    frequency base, finite and > 0 (Qwen2.5 uses 1e6)
+ */
+ps_status ps_rope_reshape_and_cache(const void *q, void *q_out, const void *k, const void *v,
+                                    const int32_t *positions, const int32_t *slot_mapping,
+                                    int32_t num_tokens, int32_t num_q_heads, double rope_theta,
+                                    const ps_pool *pool, void *stream);
 
 const char *ps_status_string(ps_status status);
 

@@ -32,8 +32,8 @@ PS_PLAN_DEFAULT, PS_PLAN_ALL_DECODE, PS_PLAN_ALL_PREFILL = 0, 1, 2
 EXPORTED = [
     "ps_plan_step", "ps_plan_sizes", "ps_plan_upload", "ps_plan_device_arrays",
     "ps_plan_host_arrays", "ps_plan_get_info", "ps_plan_destroy", "ps_reshape_and_cache",
-    "ps_paged_attention", "ps_copy_blocks", "ps_status_string", "ps_last_error_message",
-    "ps_abi_version",
+    "ps_paged_attention", "ps_copy_blocks", "ps_rope_reshape_and_cache", "ps_status_string",
+    "ps_last_error_message", "ps_abi_version",
 ]
 
 
@@ -48,7 +48,8 @@ class ps_pool(ctypes.Structure):
 class ps_step_arrays(ctypes.Structure):
     _fields_ = [("slot_mapping", ctypes.c_void_p), ("block_tables", ctypes.c_void_p),
                 ("block_table_stride", ctypes.c_int32), ("query_start_loc", ctypes.c_void_p),
-                ("num_computed_tokens", ctypes.c_void_p), ("context_lens", ctypes.c_void_p)]
+                ("num_computed_tokens", ctypes.c_void_p), ("context_lens", ctypes.c_void_p),
+                ("positions", ctypes.c_void_p)]
 
 
 class ps_plan_info(ctypes.Structure):
@@ -101,6 +102,9 @@ lib.ps_paged_attention.argtypes = [_vp, ctypes.POINTER(ps_pool), _vp, ctypes.c_i
                                    ctypes.c_float, _vp, _vp, _sz, _vp]
 lib.ps_copy_blocks.restype = ctypes.c_int32
 lib.ps_copy_blocks.argtypes = [ctypes.POINTER(ps_pool), ctypes.POINTER(ps_pool), _vp, _vp, ctypes.c_int32, _vp]
+lib.ps_rope_reshape_and_cache.restype = ctypes.c_int32
+lib.ps_rope_reshape_and_cache.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_double, ctypes.POINTER(ps_pool), _vp]
 lib.ps_status_string.restype = ctypes.c_char_p
 lib.ps_status_string.argtypes = [ctypes.c_int32]
 lib.ps_last_error_message.restype = ctypes.c_char_p
@@ -207,7 +211,8 @@ def ps_plan_host_arrays(plan: Plan, num_seqs: int, num_tokens: int) -> dict:
                 num_seqs, a.block_table_stride),
             "query_start_loc": view(a.query_start_loc, num_seqs + 1),
             "num_computed_tokens": view(a.num_computed_tokens, num_seqs),
-            "context_lens": view(a.context_lens, num_seqs)}
+            "context_lens": view(a.context_lens, num_seqs),
+            "positions": view(a.positions, num_tokens)}
 
 
 def ps_plan_get_info(plan: Plan) -> dict:
@@ -234,6 +239,13 @@ def ps_paged_attention(q, pool: ps_pool, block_tables, block_table_stride: int, 
 def ps_copy_blocks(src: ps_pool, dst: ps_pool, src_blocks, dst_blocks, num_pairs: int, stream=None):
     _check(lib.ps_copy_blocks(ctypes.byref(src), ctypes.byref(dst), _ptr(src_blocks), _ptr(dst_blocks),
                               num_pairs, _stream(stream)))
+
+
+def ps_rope_reshape_and_cache(q, q_out, k, v, positions, slot_mapping, num_tokens: int,
+                              num_q_heads: int, rope_theta: float, pool: ps_pool, stream=None):
+    _check(lib.ps_rope_reshape_and_cache(_ptr(q), _ptr(q_out), _ptr(k), _ptr(v), _ptr(positions),
+                                         _ptr(slot_mapping), num_tokens, num_q_heads, float(rope_theta),
+                                         ctypes.byref(pool), _stream(stream)))
 
 
 def ps_abi_version() -> int:

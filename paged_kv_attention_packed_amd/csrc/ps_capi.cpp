@@ -1,5 +1,7 @@
-// C ABI glue: error reporting, status strings and the scatter entry point.
+// C ABI glue: error reporting, status strings, the scatter entry points
+// (plain and with rotary embedding) and the block copy.
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 
@@ -33,10 +35,9 @@ extern "C" const char *ps_status_string(ps_status status) {
 
 extern "C" int32_t ps_abi_version(void) { return PS_ABI_VERSION; }
 
-extern "C" ps_status ps_reshape_and_cache(const void *k, const void *v, const int32_t *slot_mapping,
-                                          int32_t num_tokens, const ps_pool *pool, void *stream) {
+// Checks shared by the calls that write one layer of the pool.
+static ps_status check_cache_pool(const ps_pool *pool) {
     if (!pool) return ps_fail(PS_ERR_INVALID_ARGUMENT, "pool is NULL");
-    if (num_tokens < 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_tokens < 0");
     if (pool->block_size != PS_BLOCK)
         return ps_fail(PS_ERR_UNSUPPORTED, "block_size %d (only 16 is supported)", pool->block_size);
     if (pool->head_dim != 64 && pool->head_dim != 128)
@@ -49,11 +50,63 @@ extern "C" ps_status ps_reshape_and_cache(const void *k, const void *v, const in
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", pool->layer, pool->num_layers);
     if ((int64_t)pool->num_blocks * PS_BLOCK > INT32_MAX)
         return ps_fail(PS_ERR_UNSUPPORTED, "num_blocks %d: slots exceed int32", pool->num_blocks);
+    return PS_OK;
+}
+
+extern "C" ps_status ps_reshape_and_cache(const void *k, const void *v, const int32_t *slot_mapping,
+                                          int32_t num_tokens, const ps_pool *pool, void *stream) {
+    const ps_status st = check_cache_pool(pool);
+    if (st != PS_OK) return st;
+    if (num_tokens < 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_tokens < 0");
     if (num_tokens == 0) return PS_OK;
     if (!k || !v || !slot_mapping || !pool->k || !pool->v)
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "a device pointer is NULL");
     const int err = ps_launch_scatter(k, v, slot_mapping, num_tokens, pool, stream);
     if (err != 0) return ps_fail(PS_ERR_HIP, "scatter launch: %s", ps_hip_error_string(err));
+    return PS_OK;
+}
+
+extern "C" ps_status ps_rope_reshape_and_cache(const void *q, void *q_out, const void *k, const void *v,
+                                               const int32_t *positions, const int32_t *slot_mapping,
+                                               int32_t num_tokens, int32_t num_q_heads, double rope_theta,
+                                               const ps_pool *pool, void *stream) {
+    const ps_status st = check_cache_pool(pool);
+    if (st != PS_OK) return st;
+    if (num_tokens < 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_tokens < 0");
+    if (num_q_heads < 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_q_heads < 0");
+    if (!(rope_theta > 0.0) || !std::isfinite(rope_theta))
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "rope_theta must be finite and > 0");
+    if (num_tokens == 0) return PS_OK;
+    if (!k || !v || !positions || !slot_mapping || !pool->k || !pool->v)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "a device pointer is NULL");
+    const int D = pool->head_dim;
+    const int64_t elt = pool->dtype == PS_F32 ? 4 : 2;
+    if (num_q_heads > 0) {
+        if (!q || !q_out) return ps_fail(PS_ERR_INVALID_ARGUMENT, "q or q_out is NULL");
+        const uintptr_t n = (uintptr_t)((int64_t)num_tokens * num_q_heads * D * elt);
+        const uintptr_t a0 = (uintptr_t)q, b0 = (uintptr_t)q_out;
+        if (a0 != b0 && a0 < b0 + n && b0 < a0 + n)
+            return ps_fail(PS_ERR_INVALID_ARGUMENT, "q and q_out overlap without being equal");
+    }
+    ps_rope_launch a{};
+    a.q = q;
+    a.q_out = q_out;
+    a.k = k;
+    a.v = v;
+    a.positions = positions;
+    a.slots = slot_mapping;
+    const int64_t layer_bytes = (int64_t)pool->num_blocks * PS_BLOCK * pool->num_kv_heads * D * elt;
+    a.pool_k = static_cast<uint8_t *>(pool->k) + pool->layer * layer_bytes;
+    a.pool_v = static_cast<uint8_t *>(pool->v) + pool->layer * layer_bytes;
+    a.num_tokens = num_tokens;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = pool->num_kv_heads;
+    a.head_dim = D;
+    a.dtype = pool->dtype;
+    a.num_slots = pool->num_blocks * PS_BLOCK;
+    for (int j = 0; j < D / 2; ++j) a.inv_freq[j] = std::pow(rope_theta, -2.0 * j / D);
+    const int err = ps_launch_rope_cache(a, stream);
+    if (err != 0) return ps_fail(PS_ERR_HIP, "rope launch: %s", ps_hip_error_string(err));
     return PS_OK;
 }
 

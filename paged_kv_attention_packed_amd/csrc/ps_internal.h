@@ -95,12 +95,35 @@ struct ps_attn_launch {
     float scale_log2;       // softmax scale * log2(e)
 };
 
-// Kernel launchers (ps_kernels.hip). Return hipError_t as int.
+// Rotary embedding + KV scatter launch (ps_rope.hip). The pair frequencies
+// travel by value in the kernel arguments, so the call needs no device
+// buffer of its own.
+constexpr int PS_ROPE_MAX_HALF = 64;  // head_dim / 2 for head_dim <= 128
+struct ps_rope_launch {
+    const void *q;
+    void *q_out;
+    const void *k;
+    const void *v;
+    const int32_t *positions;
+    const int32_t *slots;
+    void *pool_k;            // this layer's K block array
+    void *pool_v;
+    int32_t num_tokens;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t dtype;
+    int32_t num_slots;       // num_blocks * 16
+    double inv_freq[PS_ROPE_MAX_HALF];  // theta^(-2j/D), j < head_dim / 2
+};
+
+// Kernel launchers (ps_kernels.hip, ps_rope.hip). Return hipError_t as int.
 int ps_launch_scatter(const void *k, const void *v, const int32_t *slot_mapping,
                       int32_t num_tokens, const ps_pool *pool, void *stream);
 int ps_launch_attention(const ps_attn_launch &a, void *stream);
 int ps_launch_copy_blocks(const ps_pool *src, const ps_pool *dst, const int32_t *src_blocks,
                           const int32_t *dst_blocks, int32_t num_pairs, void *stream);
+int ps_launch_rope_cache(const ps_rope_launch &a, void *stream);
 const char *ps_hip_error_string(int err);
 
 // Set the calling thread's error message (ps_capi.cpp).

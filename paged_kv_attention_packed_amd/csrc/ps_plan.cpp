@@ -26,7 +26,7 @@ struct ps_plan {
     int32_t n_dec = 0, n_pre = 0, n_mrg = 0;
     // the metadata blob, laid out exactly as it is copied to the device
     std::vector<uint8_t> blob;
-    size_t off_qsl = 0, off_nc = 0, off_ctx = 0, off_slot = 0, off_bt = 0;
+    size_t off_qsl = 0, off_nc = 0, off_ctx = 0, off_slot = 0, off_pos = 0, off_bt = 0;
     size_t off_dec = 0, off_pre = 0, off_mrg = 0;
     void *dev = nullptr;
     ps_plan_info info{};
@@ -262,6 +262,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         p->off_nc = take(sizeof(int32_t) * S);
         p->off_ctx = take(sizeof(int32_t) * S);
         p->off_slot = take(sizeof(int32_t) * (size_t)T);
+        p->off_pos = take(sizeof(int32_t) * (size_t)T);
         p->off_bt = take(sizeof(int32_t) * (size_t)S * p->bt_stride);
         p->off_dec = take(sizeof(ps_item) * dec.size());
         p->off_pre = take(sizeof(ps_item) * pre.size());
@@ -272,6 +273,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         int32_t *nc = p->host<int32_t>(p->off_nc);
         int32_t *ctxl = p->host<int32_t>(p->off_ctx);
         int32_t *slot = p->host<int32_t>(p->off_slot);
+        int32_t *posn = p->host<int32_t>(p->off_pos);
         int32_t *bt = p->host<int32_t>(p->off_bt);
         qsl[0] = 0;
         for (int32_t s = 0; s < S; ++s) {
@@ -283,6 +285,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
             for (int32_t i = 0; i < q_lens[s]; ++i) {
                 const int64_t pos = (int64_t)nc[s] + i;
                 slot[qsl[s] + i] = row[pos / PS_BLOCK] * PS_BLOCK + (int32_t)(pos % PS_BLOCK);
+                posn[qsl[s] + i] = (int32_t)pos;
             }
         }
         if (!dec.empty()) std::memcpy(p->host<ps_item>(p->off_dec), dec.data(), sizeof(ps_item) * dec.size());
@@ -360,6 +363,7 @@ static void fill_arrays(const ps_plan *p, const uint8_t *base, ps_step_arrays *a
     a->query_start_loc = reinterpret_cast<const int32_t *>(base + p->off_qsl);
     a->num_computed_tokens = reinterpret_cast<const int32_t *>(base + p->off_nc);
     a->context_lens = reinterpret_cast<const int32_t *>(base + p->off_ctx);
+    a->positions = reinterpret_cast<const int32_t *>(base + p->off_pos);
 }
 
 extern "C" ps_status ps_plan_device_arrays(const ps_plan *plan, ps_step_arrays *arrays) {

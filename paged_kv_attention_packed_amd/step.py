@@ -28,6 +28,12 @@ class PackedStep:
     def reshape_and_cache(self, k, v, pool: B.ps_pool, stream=None):
         B.ps_reshape_and_cache(k, v, self.arrays.slot_mapping, self.num_tokens, pool, stream)
 
+    def rope_reshape_and_cache(self, q, q_out, k, v, pool: B.ps_pool, rope_theta: float, stream=None):
+        """Rotate q (into q_out) and k at the plan's positions, then cache k and v."""
+        a = self.arrays
+        B.ps_rope_reshape_and_cache(q, q_out, k, v, a.positions, a.slot_mapping, self.num_tokens,
+                                    self.num_q_heads, rope_theta, pool, stream)
+
     def attention(self, q, pool: B.ps_pool, out, scale: float, stream=None):
         a = self.arrays
         B.ps_paged_attention(q, pool, a.block_tables, a.block_table_stride, a.query_start_loc,
@@ -35,7 +41,12 @@ class PackedStep:
                              self.num_tokens, self.num_q_heads, scale, self.plan, self.ws,
                              self.ws_bytes, stream)
 
-    def run(self, q, k, v, pool: B.ps_pool, out, scale: float, stream=None):
-        """The whole step: scatter this step's K/V, then attend."""
-        self.reshape_and_cache(k, v, pool, stream)
+    def run(self, q, k, v, pool: B.ps_pool, out, scale: float, stream=None, rope_theta=None):
+        """The whole step: scatter this step's K/V, then attend. With
+        ``rope_theta`` q and k arrive unrotated: q is rotated in place and k
+        on its way into the pool."""
+        if rope_theta is None:
+            self.reshape_and_cache(k, v, pool, stream)
+        else:
+            self.rope_reshape_and_cache(q, q, k, v, pool, rope_theta, stream)
         self.attention(q, pool, out, scale, stream)

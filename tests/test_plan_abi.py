@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert declared == set(B.EXPORTED), declared ^ set(B.EXPORTED)
     for name in declared:
         assert hasattr(B.lib, name), name
-    assert P.ps_abi_version() == 1
+    assert P.ps_abi_version() == int(re.search(r"#define PS_ABI_VERSION (\d+)", header).group(1))
 
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
@@ -46,11 +46,14 @@ def test_planner_arrays_match_oracle_slot_formula(idx):
     np.testing.assert_array_equal(h["num_computed_tokens"], nc)
     np.testing.assert_array_equal(h["context_lens"], nc + ql)
     np.testing.assert_array_equal(h["block_tables"], st.block_tables)
-    expect = []
+    expect, positions = [], []
     for s in range(st.num_seqs):
         for i in range(int(ql[s])):
             expect.append(oracle.slot(st.block_tables[s], int(nc[s]) + i))
+            positions.append(int(nc[s]) + i)
     np.testing.assert_array_equal(h["slot_mapping"], np.array(expect, dtype=np.int32))
+    # explicit position of each packed token (PageServe "01 Scheduler loop", Pack)
+    np.testing.assert_array_equal(h["positions"], np.array(positions, dtype=np.int32))
     assert len(set(expect)) == len(expect)
 
 
@@ -171,6 +174,34 @@ def test_scatter_argument_errors():
     _expect_error(B.PS_ERR_UNSUPPORTED, P.ps_reshape_and_cache, 1, 1, 1, 4, bad)
     # zero tokens is a no-op even with NULL pointers
     P.ps_reshape_and_cache(0, 0, 0, 0, pool)
+
+
+def test_rope_scatter_argument_errors():
+    pool = P.ps_pool(1 << 20, 1 << 21, 1, 8, 16, 2, 64, P.PS_F16, 0)
+    INV, UNS = B.PS_ERR_INVALID_ARGUMENT, B.PS_ERR_UNSUPPORTED
+    args = dict(q=1 << 22, q_out=1 << 23, k=1 << 24, v=1 << 25, positions=1 << 26,
+                slot_mapping=1 << 27, num_tokens=4, num_q_heads=4, rope_theta=1e6, pool=pool)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        P.ps_rope_reshape_and_cache(**a)
+
+    _expect_error(INV, call, num_tokens=-1, match="num_tokens")
+    _expect_error(INV, call, num_q_heads=-1, match="num_q_heads")
+    for theta in (0.0, -1.0, float("nan"), float("inf")):
+        _expect_error(INV, call, rope_theta=theta, match="rope_theta")
+    _expect_error(INV, call, positions=0, match="NULL")
+    _expect_error(INV, call, k=0, match="NULL")
+    _expect_error(INV, call, q=0, match="q or q_out")
+    # 4 tokens x 4 heads x 64 x 2 bytes = 2048 bytes: q_out 1 KiB past q overlaps it
+    _expect_error(INV, call, q_out=(1 << 22) + 1024, match="overlap")
+    bad = P.ps_pool(1 << 20, 1 << 21, 1, 8, 16, 2, 96, P.PS_F16, 0)
+    _expect_error(UNS, call, pool=bad, match="head_dim")
+    bad = P.ps_pool(1 << 20, 1 << 21, 1, 8, 16, 2, 64, P.PS_F16, 1)
+    _expect_error(INV, call, pool=bad, match="layer")
+    # zero tokens is a no-op even with NULL pointers
+    P.ps_rope_reshape_and_cache(0, 0, 0, 0, 0, 0, 0, 4, 1e4, pool)
 
 
 def test_split_plan_depends_only_on_logical_lengths():
