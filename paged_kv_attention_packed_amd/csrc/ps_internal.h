@@ -114,6 +114,7 @@ struct ps_rope_launch {
     int32_t head_dim;
     int32_t dtype;
     int32_t num_slots;       // num_blocks * 16
+    int32_t tokens_per_wg;   // set by the launcher
     double inv_freq[PS_ROPE_MAX_HALF];  // theta^(-2j/D), j < head_dim / 2
 };
 

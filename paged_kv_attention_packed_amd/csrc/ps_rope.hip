@@ -13,12 +13,15 @@
 // fp32 angle alone would be off by more than a bf16 ulp; the rotation
 // itself is fp32 and the result is rounded to the storage type.
 //
-// Work split: a workgroup of 256 threads owns 512 / D tokens, so that its
-// tokens' D/2 angles each come to one thread. Each thread computes one
-// (cos, sin) pair into LDS; then every head of those tokens is handled 16
-// bytes per half-row per thread: a thread loads the chunk at d and the
-// chunk at d + D/2, rotates, and stores both (eight threads cover the two
-// 128-byte halves of a bf16 head of 128). V rows move as 16-byte words.
+// Work split: a workgroup of 256 threads owns as many tokens as keep every
+// thread at <= 2 units, a unit being a 16-byte chunk at d and its partner
+// at d + D/2 of one q or k head (eight threads cover the two 128-byte
+// halves of a bf16 head of 128), or one 16-byte word of a v row. A thread
+// issues all of its loads up front, then computes up to two of the
+// tokens' (cos, sin) pairs into LDS while those loads are in flight, and
+// only then rotates and stores: one memory round trip per thread, with
+// the fp64 angle math hidden under it. q_out may alias q: a thread reads
+// and writes only its own chunks, reads first.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -79,84 +82,125 @@ __device__ inline u32x4 pack(const float *y, RBF16) {
     return w;
 }
 
+// Units a thread owns: a unit is one (head, 16-byte chunk) pair of a q or k
+// row to rotate, or one 16-byte word of a v row to copy.
+constexpr int kUnitsPerThread = 2;
+// Angles a thread computes: tokens_per_wg * D / 2 <= 512.
+constexpr int kAnglesPerThread = 2;
+
 template <class DT, int D>
 __global__ __launch_bounds__(256) void ps_rope_cache_kernel(const ps_rope_launch a) {
     constexpr int HALF = D / 2;
     constexpr int CH = 16 / DT::ELT;   // elements per 16-byte chunk
     constexpr int HC = HALF / CH;      // chunks per half row
-    constexpr int TPB = 512 / D;       // tokens per workgroup: TPB * HALF = 256 angles
-    __shared__ float2 cs[TPB][HALF];
+    constexpr int ROW_W = D / CH;      // 16-byte words per head row
+    __shared__ float2 cs[kAnglesPerThread * 256];
 
-    const int t0 = blockIdx.x * TPB;
-    const int n_tok = min(TPB, a.num_tokens - t0);
-    {
-        const int tok = threadIdx.x / HALF, j = threadIdx.x % HALF;
-        float c = 1.f, s = 0.f;
-        if (tok < n_tok) {
-            const double ang = (double)a.positions[t0 + tok] * a.inv_freq[j];
-            double sd, cd;
-            sincos(ang, &sd, &cd);
-            c = (float)cd;
-            s = (float)sd;
-        }
-        cs[tok][j] = make_float2(c, s);
-    }
-    __syncthreads();
-
+    const int tpb = a.tokens_per_wg;
+    const int64_t t0 = (int64_t)blockIdx.x * tpb;
+    const int n_tok = (int)min<int64_t>(tpb, a.num_tokens - t0);
     const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-    const int rot_units = (Hq + Hkv) * HC;    // (head, chunk) pairs to rotate per token
-    const int v_words = Hkv * D / CH;         // 16-byte words of one token's V row
+    const int q_units = Hq * HC;
+    const int rot_units = (Hq + Hkv) * HC;
+    const int v_words = Hkv * ROW_W;
     const int per_tok = rot_units + v_words;
+    const int n_units = n_tok * per_tok;
+    const int n_angles = n_tok * HALF;
+
+    // 1. positions first, so that the angle math below can start while the
+    //    data loads are still in flight. Loads are branch-free: indexes are
+    //    clamped into range and the unused results ignored, so that no
+    //    load waits on another at a control-flow join.
+    int32_t pos[kAnglesPerThread];
+    double freq[kAnglesPerThread];
+#pragma unroll
+    for (int i = 0; i < kAnglesPerThread; ++i) {
+        const int idx = min((int)threadIdx.x + 256 * i, n_angles - 1);
+        pos[i] = a.positions[t0 + idx / HALF];
+        freq[i] = a.inv_freq[idx % HALF];
+    }
+
+    // 2. every load of this thread's units
     const u32x4 *q = static_cast<const u32x4 *>(a.q);
-    u32x4 *q_out = static_cast<u32x4 *>(a.q_out);
     const u32x4 *k = static_cast<const u32x4 *>(a.k);
     const u32x4 *v = static_cast<const u32x4 *>(a.v);
-    u32x4 *pk = static_cast<u32x4 *>(a.pool_k);
-    u32x4 *pv = static_cast<u32x4 *>(a.pool_v);
-    constexpr int ROW_W = D / CH;             // 16-byte words per head row
-
-    for (int u = threadIdx.x; u < n_tok * per_tok; u += 256) {
+    u32x4 lo[kUnitsPerThread], hi[kUnitsPerThread];
+    int32_t slot[kUnitsPerThread];
+    int kind[kUnitsPerThread];      // 0 none, 1 q, 2 k, 3 v
+    int64_t dst[kUnitsPerThread];   // word index of the destination (k, v: within the slot row)
+    int cbase[kUnitsPerThread];     // first angle of the chunk in cs
+#pragma unroll
+    for (int i = 0; i < kUnitsPerThread; ++i) {
+        const int u0 = threadIdx.x + 256 * i;
+        const int u = min(u0, n_units - 1);
         const int tok = u / per_tok;
         const int r = u - tok * per_tok;
         const int64_t t = t0 + tok;
-        if (r < rot_units) {
-            const int head = r / HC, c = r - head * HC;
-            const u32x4 *src;
-            u32x4 *dst;
-            if (head < Hq) {
-                src = q + (t * Hq + head) * ROW_W;
-                dst = q_out + (t * Hq + head) * ROW_W;
-            } else {
-                const int32_t slot = a.slots[t];
-                if ((uint32_t)slot >= (uint32_t)a.num_slots) continue;
-                src = k + (t * Hkv + (head - Hq)) * ROW_W;
-                dst = pk + ((int64_t)slot * Hkv + (head - Hq)) * ROW_W;
-            }
-            const u32x4 lo = src[c], hi = src[HC + c];
-            float x1[CH], x2[CH], y1[CH], y2[CH];
-            unpack(lo, x1, DT{});
-            unpack(hi, x2, DT{});
+        const bool rot = r < rot_units;
+        const int head = r / HC;
+        const int c = r - head * HC;
+        const bool isq = head < Hq;
+        const int64_t qw = (t * Hq + head) * ROW_W + c;
+        const int64_t kw = (t * Hkv + (head - Hq)) * ROW_W + c;
+        const int64_t vw = t * v_words + (r - rot_units);
+        const u32x4 *src = rot ? (isq ? q + qw : k + kw) : v + vw;
+        slot[i] = a.slots[t];
+        lo[i] = src[0];
+        hi[i] = src[rot ? HC : 0];
+        kind[i] = u0 >= n_units ? 0 : rot ? (isq ? 1 : 2) : 3;
+        dst[i] = rot ? (isq ? qw : (int64_t)(head - Hq) * ROW_W + c) : (int64_t)(r - rot_units);
+        cbase[i] = tok * HALF + c * CH;
+    }
+
+    // 3. cos / sin of this workgroup's angles (fp64), shared through LDS
 #pragma unroll
-            for (int e = 0; e < CH; ++e) {
-                const float2 f = cs[tok][c * CH + e];
-                y1[e] = x1[e] * f.x - x2[e] * f.y;
-                y2[e] = x2[e] * f.x + x1[e] * f.y;
-            }
-            dst[c] = pack(y1, DT{});
-            dst[HC + c] = pack(y2, DT{});
-        } else {
-            const int32_t slot = a.slots[t];
-            if ((uint32_t)slot >= (uint32_t)a.num_slots) continue;
-            const int w = r - rot_units;
-            pv[(int64_t)slot * v_words + w] = v[t * v_words + w];
+    for (int i = 0; i < kAnglesPerThread; ++i) {
+        const int idx = threadIdx.x + 256 * i;
+        if (idx < n_angles) {
+            double sd, cd;
+            sincos((double)pos[i] * freq[i], &sd, &cd);
+            cs[idx] = make_float2((float)cd, (float)sd);
         }
+    }
+    __syncthreads();
+
+    // 4. rotate and store
+    u32x4 *q_out = static_cast<u32x4 *>(a.q_out);
+    u32x4 *pk = static_cast<u32x4 *>(a.pool_k);
+    u32x4 *pv = static_cast<u32x4 *>(a.pool_v);
+    const uint32_t num_slots = (uint32_t)a.num_slots;
+#pragma unroll
+    for (int i = 0; i < kUnitsPerThread; ++i) {
+        if (kind[i] == 0) continue;
+        if (kind[i] != 1 && (uint32_t)slot[i] >= num_slots) continue;
+        if (kind[i] == 3) {
+            pv[(int64_t)slot[i] * v_words + dst[i]] = lo[i];
+            continue;
+        }
+        float x1[CH], x2[CH], y1[CH], y2[CH];
+        unpack(lo[i], x1, DT{});
+        unpack(hi[i], x2, DT{});
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+            const float2 f = cs[cbase[i] + e];
+            y1[e] = x1[e] * f.x - x2[e] * f.y;
+            y2[e] = x2[e] * f.x + x1[e] * f.y;
+        }
+        u32x4 *o = kind[i] == 1 ? q_out + dst[i] : pk + (int64_t)slot[i] * v_words + dst[i];
+        o[0] = pack(y1, DT{});
+        o[HC] = pack(y2, DT{});
     }
 }
 
 template <class DT, int D>
-hipError_t launch_t(const ps_rope_launch &a, hipStream_t st) {
-    constexpr int TPB = 512 / D;
-    const unsigned grid = (unsigned)((a.num_tokens + TPB - 1) / TPB);
+hipError_t launch_t(ps_rope_launch a, hipStream_t st) {
+    constexpr int CH = 16 / DT::ELT;
+    const int per_tok = (a.num_q_heads + a.num_kv_heads) * (D / 2 / CH) + a.num_kv_heads * (D / CH);
+    int tpb = kUnitsPerThread * 256 / per_tok;
+    tpb = tpb < 1 ? 1 : tpb;
+    tpb = tpb > kAnglesPerThread * 256 / (D / 2) ? kAnglesPerThread * 256 / (D / 2) : tpb;
+    a.tokens_per_wg = tpb;
+    const unsigned grid = (unsigned)((a.num_tokens + tpb - 1) / tpb);
     hipLaunchKernelGGL((ps_rope_cache_kernel<DT, D>), dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
 }
