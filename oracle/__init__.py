@@ -15,7 +15,8 @@ PageServe "01 Scheduler loop" (Pack / Execute, System architecture),
 phase 8 (one packed [1, T] pass); tinyserve README "How it works" (two
 K/V slabs, block tables, stepped causal mask for verify rows) and
 "Highlights" (grouped-query attention, rotary embeddings of the Qwen2
-forward pass).
+forward pass), tinyserve README "How it works" (rejection-sampling
+verification of speculative drafts).
 """
 from __future__ import annotations
 
@@ -69,6 +70,10 @@ def _load():
     lib.oracle_rope.restype = None
     lib.oracle_rope.argtypes = [_f64p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _i32p,
                                 ctypes.c_double, _f64p]
+    _f32p = ctypes.POINTER(ctypes.c_float)
+    lib.oracle_spec_verify.restype = None
+    lib.oracle_spec_verify.argtypes = [_f32p, _f32p, _i32p, _i32p, _f64p, _f64p, ctypes.c_int32,
+                                       ctypes.c_int32, _i32p, _i32p]
     lib.oracle_num_threads.restype = ctypes.c_int32
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -223,3 +228,36 @@ def rope(x, positions, theta: float):
         _load().oracle_rope(_ptr(x, ctypes.c_double), T, H, D, _ptr(pos, ctypes.c_int32),
                             float(theta), _ptr(out, ctypes.c_double))
     return out
+
+
+def spec_verify(target_probs, draft_probs, draft_tokens, draft_start, accept_u, sample_u):
+    """Rejection-sampling verification of speculative rounds (see oracle.c).
+
+    target_probs [total_drafts + S, V] fp32, draft_probs [total_drafts, V]
+    fp32, draft_tokens [total_drafts], draft_start [S + 1] (exclusive prefix
+    sum of the per-sequence draft counts), accept_u [total_drafts] and
+    sample_u [S] fp64 uniforms. Returns (num_accepted [S], next_token [S]).
+    """
+    tp = np.ascontiguousarray(target_probs, dtype=np.float32)
+    dp = np.ascontiguousarray(draft_probs, dtype=np.float32)
+    dt = _i32(draft_tokens)
+    ds = _i32(draft_start)
+    au = np.ascontiguousarray(accept_u, dtype=np.float64)
+    su = np.ascontiguousarray(sample_u, dtype=np.float64)
+    S = len(ds) - 1
+    V = tp.shape[1]
+    assert tp.ndim == 2 and (dp.size == 0 or dp.shape[1] == V)
+    assert len(su) == S
+    na = np.empty(S, dtype=np.int32)
+    nt = np.empty(S, dtype=np.int32)
+    if S == 0:
+        return na, nt
+    # zero-length arrays still need a valid pointer
+    dp = dp if dp.size else np.zeros((1, V), np.float32)
+    dt = dt if dt.size else np.zeros(1, np.int32)
+    au = au if au.size else np.zeros(1)
+    _load().oracle_spec_verify(_ptr(tp, ctypes.c_float), _ptr(dp, ctypes.c_float), _ptr(dt, ctypes.c_int32),
+                               _ptr(ds, ctypes.c_int32), _ptr(au, ctypes.c_double),
+                               _ptr(su, ctypes.c_double), S, V, _ptr(na, ctypes.c_int32),
+                               _ptr(nt, ctypes.c_int32))
+    return na, nt

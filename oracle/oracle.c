@@ -36,6 +36,14 @@
  *    loop" (Pack: explicit position_ids). Read as Qwen2's rotation: for
  *    j < D/2 the pair (x[j], x[j + D/2]) turns by the angle
  *    pos * theta^(-2j/D).
+ *  - speculative verification: PageServe "06 Development history" / Next
+ *    steps (rejection sampling, so speculation also serves sampled
+ *    requests) and tinyserve README "How it works" (Speculative decoding:
+ *    draft i is kept with probability min(1, p_i(d_i) / q_i(d_i)); at the
+ *    first rejection the replacement comes from normalize(max(p_i - q_i,
+ *    0)); when every draft survives a bonus token comes from the last
+ *    target distribution). The random numbers are inputs: one uniform per
+ *    draft for its acceptance and one per sequence for the final draw.
  *
  * Everything is fp64; inputs arrive already rounded to the storage dtype
  * and upcast by the caller.
@@ -268,6 +276,109 @@ void oracle_rope(const double *x, int64_t T, int32_t H, int32_t D, const int32_t
             }
         }
     }
+}
+
+/*
+ * One categorical draw by inverse CDF. Weights are taken at fixed point:
+ * w_int[t] = floor(clamp(w[t], 0, 1) * 2^40) (NaN counts as 0), so the
+ * running sums are exact integers and do not depend on summation order.
+ * With total = sum_t w_int[t] and v53 = floor(clamp(v, 0, 1 - 2^-53) * 2^53),
+ * the draw is the smallest t whose running sum exceeds
+ * floor(v53 * total / 2^53). Returns -1 when total is 0.
+ */
+static uint64_t fixed_weight(double w)
+{
+    if (!(w > 0.0)) return 0;
+    if (w > 1.0) w = 1.0;
+    return (uint64_t)(w * 1099511627776.0); /* 2^40 */
+}
+
+static uint64_t uniform53(double v)
+{
+    if (!(v > 0.0)) return 0;
+    const uint64_t top = ((uint64_t)1 << 53) - 1;
+    if (v >= 1.0) return top;
+    const uint64_t x = (uint64_t)(v * 9007199254740992.0); /* 2^53 */
+    return x > top ? top : x;
+}
+
+static int32_t categorical_draw(const double *w, int32_t n, double v)
+{
+    uint64_t total = 0;
+    for (int32_t t = 0; t < n; ++t) total += fixed_weight(w[t]);
+    if (total == 0) return -1;
+    const uint64_t target = (uint64_t)(((unsigned __int128)uniform53(v) * total) >> 53);
+    uint64_t run = 0;
+    for (int32_t t = 0; t < n; ++t) {
+        run += fixed_weight(w[t]);
+        if (run > target) return t;
+    }
+    return -1; /* unreachable: target < total */
+}
+
+/*
+ * Rejection-sampling verification of a batch of speculative rounds.
+ *
+ * Sequence s proposed k_s = draft_start[s + 1] - draft_start[s] drafts
+ * d_0..d_{k_s - 1} (draft_tokens[draft_start[s] + i]); q_i
+ * (draft_probs row draft_start[s] + i) is the distribution d_i was drawn
+ * from and p_i (target_probs row draft_start[s] + s + i) the target's
+ * distribution at the same position; p_{k_s} is the target's distribution
+ * after the last draft. Rows are vocab entries long.
+ *
+ * For i = 0, 1, ...: d_i is kept when accept_u[draft_start[s] + i] * q_i(d_i)
+ * < p_i(d_i) (probability min(1, p_i(d_i) / q_i(d_i)) for a uniform in
+ * [0, 1)). At the first rejection the next token is drawn with sample_u[s]
+ * from max(p_i - q_i, 0) (elementwise, fp64), or from p_i if that residual
+ * has no mass at the draw's resolution; if no draft is rejected it is
+ * drawn from p_{k_s}. Outputs: num_accepted[s] (drafts kept) and
+ * next_token[s] (-1 if the distribution drawn from has no mass). A
+ * sequence with k_s < 0 or a draft token outside [0, vocab) gets -1 in
+ * both outputs.
+ */
+void oracle_spec_verify(const float *target_probs, const float *draft_probs,
+                        const int32_t *draft_tokens, const int32_t *draft_start,
+                        const double *accept_u, const double *sample_u,
+                        int32_t num_seqs, int32_t vocab,
+                        int32_t *num_accepted, int32_t *next_token)
+{
+    double *w = (double *)malloc(sizeof(double) * (size_t)(vocab > 0 ? vocab : 1));
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int64_t d0 = draft_start[s];
+        const int32_t k = draft_start[s + 1] - draft_start[s];
+        int bad = k < 0;
+        for (int32_t i = 0; !bad && i < k; ++i)
+            bad = draft_tokens[d0 + i] < 0 || draft_tokens[d0 + i] >= vocab;
+        if (bad) {
+            num_accepted[s] = -1;
+            next_token[s] = -1;
+            continue;
+        }
+        int32_t i = 0;
+        for (; i < k; ++i) {
+            const int32_t d = draft_tokens[d0 + i];
+            const double p = target_probs[(d0 + s + i) * vocab + d];
+            const double q = draft_probs[(d0 + i) * vocab + d];
+            if (!(accept_u[d0 + i] * q < p)) break; /* rejected */
+        }
+        num_accepted[s] = i;
+        const float *prow = target_probs + (d0 + s + i) * vocab;
+        int32_t tok = -1;
+        if (i < k) {
+            const float *qrow = draft_probs + (d0 + i) * vocab;
+            for (int32_t t = 0; t < vocab; ++t) {
+                const double r = (double)prow[t] - (double)qrow[t];
+                w[t] = r > 0.0 ? r : 0.0;
+            }
+            tok = categorical_draw(w, vocab, sample_u[s]);
+        }
+        if (tok < 0) {
+            for (int32_t t = 0; t < vocab; ++t) w[t] = prow[t];
+            tok = categorical_draw(w, vocab, sample_u[s]);
+        }
+        next_token[s] = tok;
+    }
+    free(w);
 }
 
 /* Threads the OpenMP runtime will use for oracle_attention. */
