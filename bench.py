@@ -61,10 +61,14 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="time steps as individual launches instead of replaying them from a "
                          "captured HIP graph")
-    ap.add_argument("--op", default="step", choices=["step", "copy-blocks", "swap-blocks", "rope-cache"],
+    ap.add_argument("--op", default="step",
+                    choices=["step", "copy-blocks", "swap-blocks", "rope-cache", "spec-verify"],
                     help="step: the packed step (default); copy-blocks: copy-on-write block copies "
                          "in one device pool; swap-blocks: blocks out to a pinned host pool and back; "
-                         "rope-cache: rotary embedding of the step's q and k fused with the KV scatter")
+                         "rope-cache: rotary embedding of the step's q and k fused with the KV scatter; "
+                         "spec-verify: rejection sampling over the step's verify rows (use --config 5)")
+    ap.add_argument("--proposer", default="draft", choices=["draft", "ngram"],
+                    help="spec-verify: draft-model or n-gram proposer distributions")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times): the "
                          "reference kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
@@ -282,6 +286,70 @@ def bench_rope(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_spec(args):
+    """ps_spec_verify throughput on the verify rows of the chosen step: one
+    round per sequence scheduled with 1 + k tokens, over the Qwen2.5
+    vocabulary. Copies of the probability rows rotate so that the rows a
+    call reads come from HBM."""
+    import numpy as np
+    import torch
+    import oracle  # expected outputs only: checked once after timing
+    import paged_kv_attention_packed_amd as P
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    r = workloads.spec_config(args.config, args.proposer)
+    S, V, K = r.num_seqs, r.vocab, r.total_drafts
+    if S == 0:
+        print(f"config {args.config} has no verify rows", file=sys.stderr)
+        sys.exit(2)
+    ena, ent = oracle.spec_verify(r.target_probs, r.draft_probs, r.draft_tokens, r.draft_start,
+                                  r.accept_u, r.sample_u)
+    ks = np.diff(r.draft_start)
+    rows_read = int(np.where(ena < ks, 2, 1).sum())          # rejection: p_j and q_j; else p_k
+    moved = rows_read * V * 4
+    per_copy = r.target_probs.nbytes + r.draft_probs.nbytes
+    nrot = max(1, min(64, math.ceil(ROTATE_TARGET / moved)))
+    tp0, dp0 = torch.from_numpy(r.target_probs).to(dev), torch.from_numpy(r.draft_probs).to(dev)
+    copies = [(tp0, dp0)] + [(tp0.clone(), dp0.clone()) for _ in range(nrot - 1)]
+    dt, ds = torch.from_numpy(r.draft_tokens).to(dev), torch.from_numpy(r.draft_start).to(dev)
+    au, su = torch.from_numpy(r.accept_u).to(dev), torch.from_numpy(r.sample_u).to(dev)
+    na = torch.empty(S, dtype=torch.int32, device=dev)
+    nt = torch.empty(S, dtype=torch.int32, device=dev)
+    wsb = P.ps_spec_verify_workspace_bytes(S, V)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def launch(i):
+        tp, dp = copies[i % nrot]
+        P.ps_spec_verify(tp, dp, dt, ds, au, su, S, K, V, na, nt, ws, wsb, stream)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        launch(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / args.steps * 1e-3
+    ok = bool((na.cpu().numpy() == ena).all() and (nt.cpu().numpy() == ent).all())
+    gbs = moved / t / 1e9
+    result = {"metric": "speculative verify (rejection sampling) HBM GB/s, 1 MI355X", "value": round(gbs, 1),
+              "unit": "GB/s", "us_per_call": round(t * 1e6, 2), "rounds_per_s": round(S / t, 1),
+              "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+              "matches_oracle": ok,
+              "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+              "dtype": "f32", "data": "synthetic",
+              "config": {"workload": r.name, "op": args.op, "rounds": S, "drafts": K, "vocab": V,
+                         "drafts_kept": int(ena.sum()), "rows_read": rows_read,
+                         "bytes_per_call": moved, "input_copies": nrot,
+                         "input_bytes_per_copy": per_copy}}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -290,6 +358,9 @@ def main():
         sys.exit(2)
     if args.op == "rope-cache":
         bench_rope(args)
+        return
+    if args.op == "spec-verify":
+        bench_spec(args)
         return
     if args.op != "step":
         bench_blocks(args)

@@ -32,6 +32,11 @@
  *  - Supported: block_size 16; head_dim 64 or 128; fp32, fp16, bf16
  *    storage with fp32 accumulation; num_q_heads a multiple of
  *    num_kv_heads.
+ *
+ * Around the step: ps_rope_reshape_and_cache (rotary embedding fused with
+ * the scatter, for K that arrives unrotated), ps_copy_blocks (copy-on-write
+ * and swap between device and pinned host pools) and ps_spec_verify
+ * (rejection sampling over the verify rows' distributions).
  */
 #ifndef PS_H
 #define PS_H
@@ -283,6 +288,61 @@ ps_status ps_rope_reshape_and_cache(const void *q, void *q_out, const void *k, c
                                     const int32_t *positions, const int32_t *slot_mapping,
                                     int32_t num_tokens, int32_t num_q_heads, double rope_theta,
                                     const ps_pool *pool, void *stream);
+
+/*
+ * Rejection-sampling verification of speculative drafts, for the 1 + k
+ * verify rows a packed step scores (tinyserve README, "How it works",
+ * Speculative decoding; PageServe "06 Development history", Next steps:
+ * rejection sampling, so that sampled requests can speculate too).
+ *
+ * Sequence s proposed k_s = draft_start[s + 1] - draft_start[s] drafts
+ * d_i = draft_tokens[draft_start[s] + i]. q_i, row draft_start[s] + i of
+ * draft_probs, is the distribution d_i was drawn from; p_i, row
+ * draft_start[s] + s + i of target_probs, is the target's distribution at
+ * the same position (the verify row scoring the token before d_i), and
+ * p_{k_s} the one after the last draft (rows per sequence: k_s + 1).
+ *
+ *  - Draft d_i is kept while accept_uniforms[draft_start[s] + i] * q_i(d_i)
+ *    < p_i(d_i), evaluated in fp64: kept with probability
+ *    min(1, p_i(d_i) / q_i(d_i)) for a uniform in [0, 1).
+ *  - At the first rejection (index j) the next token is drawn with
+ *    sample_uniforms[s] from max(p_j - q_j, 0) (elementwise, fp64), or
+ *    from p_j when that residual has no mass at the draw's resolution;
+ *    when every draft is kept (j = k_s) it is drawn from p_{k_s} (the
+ *    bonus token). A zero-draft sequence is a plain sampled decode.
+ *  - A draw from weights w with uniform v is the smallest t whose running
+ *    sum of floor(clamp(w, 0, 1) * 2^40) exceeds
+ *    floor(floor(clamp(v, 0, 1 - 2^-53) * 2^53) * total / 2^53), in exact
+ *    integers, so it is independent of how the vocabulary is split; NaN
+ *    weights count as 0, and weights below 2^-40 are never drawn.
+ *
+ * Outputs num_accepted[s] = j and next_token[s] (-1 if the row drawn from
+ * has no mass). A sequence whose draft_start entries are not
+ * 0 <= draft_start[s] <= draft_start[s + 1] <= total_drafts, or with a
+ * draft token outside [0, vocab_size), gets -1 in both outputs; the other
+ * sequences are unaffected.
+ *
+ *   target_probs     device fp32 [total_drafts + num_seqs, vocab_size]
+ *   draft_probs      device fp32 [total_drafts, vocab_size]
+ *   draft_tokens     device int32 [total_drafts]
+ *   draft_start      device int32 [num_seqs + 1]
+ *   accept_uniforms  device fp64 [total_drafts]
+ *   sample_uniforms  device fp64 [num_seqs]
+ *   num_accepted, next_token  device int32 [num_seqs], written
+ *   workspace        device, 8-byte aligned, at least
+ *                    ps_spec_verify_workspace_bytes(num_seqs, vocab_size)
+ *                    bytes; overwritten
+ * vocab_size is at most 2^23. draft_probs, draft_tokens and
+ * accept_uniforms may be NULL when total_drafts is 0.
+ */
+size_t ps_spec_verify_workspace_bytes(int32_t num_seqs, int32_t vocab_size);
+
+ps_status ps_spec_verify(const float *target_probs, const float *draft_probs,
+                         const int32_t *draft_tokens, const int32_t *draft_start,
+                         const double *accept_uniforms, const double *sample_uniforms,
+                         int32_t num_seqs, int32_t total_drafts, int32_t vocab_size,
+                         int32_t *num_accepted, int32_t *next_token, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 const char *ps_status_string(ps_status status);
 

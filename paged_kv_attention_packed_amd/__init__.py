@@ -9,5 +9,6 @@ from ._binding import (  # noqa: F401
     PS_BF16, PS_F16, PS_F32, PS_PLAN_ALL_DECODE, PS_PLAN_ALL_PREFILL, PS_PLAN_DEFAULT, Plan,
     PsError, make_pool, ps_abi_version, ps_copy_blocks, ps_paged_attention, ps_plan_device_arrays,
     ps_plan_get_info, ps_plan_host_arrays, ps_plan_sizes, ps_plan_step, ps_plan_upload,
-    ps_pool, ps_reshape_and_cache, ps_rope_reshape_and_cache, status_string)
+    ps_pool, ps_reshape_and_cache, ps_rope_reshape_and_cache, ps_spec_verify,
+    ps_spec_verify_workspace_bytes, status_string)
 from .step import PackedStep  # noqa: F401

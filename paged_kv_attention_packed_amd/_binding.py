@@ -32,8 +32,8 @@ PS_PLAN_DEFAULT, PS_PLAN_ALL_DECODE, PS_PLAN_ALL_PREFILL = 0, 1, 2
 EXPORTED = [
     "ps_plan_step", "ps_plan_sizes", "ps_plan_upload", "ps_plan_device_arrays",
     "ps_plan_host_arrays", "ps_plan_get_info", "ps_plan_destroy", "ps_reshape_and_cache",
-    "ps_paged_attention", "ps_copy_blocks", "ps_rope_reshape_and_cache", "ps_status_string",
-    "ps_last_error_message", "ps_abi_version",
+    "ps_paged_attention", "ps_copy_blocks", "ps_rope_reshape_and_cache", "ps_spec_verify",
+    "ps_spec_verify_workspace_bytes", "ps_status_string", "ps_last_error_message", "ps_abi_version",
 ]
 
 
@@ -105,6 +105,11 @@ lib.ps_copy_blocks.argtypes = [ctypes.POINTER(ps_pool), ctypes.POINTER(ps_pool),
 lib.ps_rope_reshape_and_cache.restype = ctypes.c_int32
 lib.ps_rope_reshape_and_cache.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_double, ctypes.POINTER(ps_pool), _vp]
+lib.ps_spec_verify_workspace_bytes.restype = ctypes.c_size_t
+lib.ps_spec_verify_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+lib.ps_spec_verify.restype = ctypes.c_int32
+lib.ps_spec_verify.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                               _vp, _vp, _vp, _sz, _vp]
 lib.ps_status_string.restype = ctypes.c_char_p
 lib.ps_status_string.argtypes = [ctypes.c_int32]
 lib.ps_last_error_message.restype = ctypes.c_char_p
@@ -246,6 +251,19 @@ def ps_rope_reshape_and_cache(q, q_out, k, v, positions, slot_mapping, num_token
     _check(lib.ps_rope_reshape_and_cache(_ptr(q), _ptr(q_out), _ptr(k), _ptr(v), _ptr(positions),
                                          _ptr(slot_mapping), num_tokens, num_q_heads, float(rope_theta),
                                          ctypes.byref(pool), _stream(stream)))
+
+
+def ps_spec_verify_workspace_bytes(num_seqs: int, vocab_size: int) -> int:
+    return lib.ps_spec_verify_workspace_bytes(num_seqs, vocab_size)
+
+
+def ps_spec_verify(target_probs, draft_probs, draft_tokens, draft_start, accept_uniforms,
+                   sample_uniforms, num_seqs: int, total_drafts: int, vocab_size: int, num_accepted,
+                   next_token, workspace, workspace_bytes: int, stream=None):
+    _check(lib.ps_spec_verify(_ptr(target_probs), _ptr(draft_probs), _ptr(draft_tokens), _ptr(draft_start),
+                              _ptr(accept_uniforms), _ptr(sample_uniforms), num_seqs, total_drafts,
+                              vocab_size, _ptr(num_accepted), _ptr(next_token), _ptr(workspace),
+                              workspace_bytes, _stream(stream)))
 
 
 def ps_abi_version() -> int:

@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libps.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["ps_capi.cpp", "ps_plan.cpp", "ps_kernels.hip", "ps_rope.hip"]
+SOURCES = ["ps_capi.cpp", "ps_plan.cpp", "ps_kernels.hip", "ps_rope.hip", "ps_spec.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -141,3 +141,53 @@ extern "C" ps_status ps_copy_blocks(const ps_pool *src, const ps_pool *dst, cons
     if (err != 0) return ps_fail(PS_ERR_HIP, "copy launch: %s", ps_hip_error_string(err));
     return PS_OK;
 }
+
+extern "C" size_t ps_spec_verify_workspace_bytes(int32_t num_seqs, int32_t vocab_size) {
+    if (num_seqs <= 0 || vocab_size <= 0) return 0;
+    return ps_spec_workspace(num_seqs, vocab_size);
+}
+
+extern "C" ps_status ps_spec_verify(const float *target_probs, const float *draft_probs,
+                                    const int32_t *draft_tokens, const int32_t *draft_start,
+                                    const double *accept_uniforms, const double *sample_uniforms,
+                                    int32_t num_seqs, int32_t total_drafts, int32_t vocab_size,
+                                    int32_t *num_accepted, int32_t *next_token, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    if (num_seqs < 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_seqs < 0");
+    if (total_drafts < 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "total_drafts < 0");
+    if (vocab_size < 1 || vocab_size > PS_SPEC_MAX_VOCAB)
+        return ps_fail(PS_ERR_UNSUPPORTED, "vocab_size %d outside [1, %d]", vocab_size, PS_SPEC_MAX_VOCAB);
+    if (num_seqs == 0) return PS_OK;
+    if (!target_probs || !draft_start || !sample_uniforms || !num_accepted || !next_token || !workspace)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "a device pointer is NULL");
+    if (total_drafts > 0 && (!draft_probs || !draft_tokens || !accept_uniforms))
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "draft_probs, draft_tokens or accept_uniforms is NULL");
+    const size_t need = ps_spec_workspace(num_seqs, vocab_size);
+    if (workspace_bytes < need)
+        return ps_fail(PS_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, the call needs %zu",
+                       workspace_bytes, need);
+    if (((uintptr_t)workspace & 7) != 0)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "workspace is not 8-byte aligned");
+    ps_spec_launch a{};
+    a.target = target_probs;
+    a.draft = draft_probs;
+    a.tokens = draft_tokens;
+    a.starts = draft_start;
+    a.accept_u = accept_uniforms;
+    a.sample_u = sample_uniforms;
+    a.num_accepted = num_accepted;
+    a.next_token = next_token;
+    a.chunk_sums = static_cast<uint64_t *>(workspace);
+    a.decisions = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) +
+                                              ps_spec_sums_bytes(num_seqs, vocab_size));
+    a.num_seqs = num_seqs;
+    a.total_drafts = total_drafts;
+    a.vocab = vocab_size;
+    a.n_chunks = (vocab_size + PS_SPEC_CHUNK - 1) / PS_SPEC_CHUNK;
+    // 16-byte loads when every row starts 16-byte aligned
+    const bool vec = vocab_size % 4 == 0 && ((uintptr_t)target_probs & 15) == 0 &&
+                     (total_drafts == 0 || ((uintptr_t)draft_probs & 15) == 0);
+    const int err = ps_launch_spec_verify(a, vec, stream);
+    if (err != 0) return ps_fail(PS_ERR_HIP, "verify launch: %s", ps_hip_error_string(err));
+    return PS_OK;
+}

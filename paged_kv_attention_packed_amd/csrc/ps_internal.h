@@ -118,13 +118,38 @@ struct ps_rope_launch {
     double inv_freq[PS_ROPE_MAX_HALF];  // theta^(-2j/D), j < head_dim / 2
 };
 
-// Kernel launchers (ps_kernels.hip, ps_rope.hip). Return hipError_t as int.
+// Speculative verification launch (ps_spec.hip).
+constexpr int PS_SPEC_CHUNK = 4096;   // vocab entries per first-pass workgroup
+constexpr int PS_SPEC_MAX_VOCAB = 1 << 23;   // fixed-point sums stay below 2^63
+struct ps_spec_launch {
+    const float *target;       // [total_drafts + num_seqs, vocab]
+    const float *draft;        // [total_drafts, vocab]
+    const int32_t *tokens;     // [total_drafts]
+    const int32_t *starts;     // [num_seqs + 1]
+    const double *accept_u;    // [total_drafts]
+    const double *sample_u;    // [num_seqs]
+    int32_t *num_accepted;     // [num_seqs]
+    int32_t *next_token;       // [num_seqs]
+    uint64_t *chunk_sums;      // workspace [num_seqs, n_chunks]
+    int32_t *decisions;        // workspace [num_seqs, 2]: drafts kept, malformed flag
+    int32_t num_seqs, total_drafts, vocab, n_chunks;
+};
+inline size_t ps_spec_sums_bytes(int64_t num_seqs, int64_t vocab) {
+    const int64_t chunks = (vocab + PS_SPEC_CHUNK - 1) / PS_SPEC_CHUNK;
+    return ps_align256((size_t)(num_seqs * chunks * sizeof(uint64_t)));
+}
+inline size_t ps_spec_workspace(int64_t num_seqs, int64_t vocab) {
+    return ps_spec_sums_bytes(num_seqs, vocab) + ps_align256((size_t)(num_seqs * 2 * sizeof(int32_t)));
+}
+
+// Kernel launchers (ps_kernels.hip, ps_rope.hip, ps_spec.hip). Return hipError_t as int.
 int ps_launch_scatter(const void *k, const void *v, const int32_t *slot_mapping,
                       int32_t num_tokens, const ps_pool *pool, void *stream);
 int ps_launch_attention(const ps_attn_launch &a, void *stream);
 int ps_launch_copy_blocks(const ps_pool *src, const ps_pool *dst, const int32_t *src_blocks,
                           const int32_t *dst_blocks, int32_t num_pairs, void *stream);
 int ps_launch_rope_cache(const ps_rope_launch &a, void *stream);
+int ps_launch_spec_verify(const ps_spec_launch &a, bool vec, void *stream);
 const char *ps_hip_error_string(int err);
 
 // Set the calling thread's error message (ps_capi.cpp).

@@ -204,6 +204,35 @@ def test_rope_scatter_argument_errors():
     P.ps_rope_reshape_and_cache(0, 0, 0, 0, 0, 0, 0, 4, 1e4, pool)
 
 
+def test_spec_verify_argument_errors():
+    INV, UNS, WS = B.PS_ERR_INVALID_ARGUMENT, B.PS_ERR_UNSUPPORTED, B.PS_ERR_WORKSPACE_TOO_SMALL
+    V, S = 151936, 32
+    ws = P.ps_spec_verify_workspace_bytes(S, V)
+    # 38 chunks of 4096 entries: one u64 sum each, then two int32 per sequence
+    assert ws == 256 * -(-(S * 38 * 8) // 256) + 256 * -(-(S * 8) // 256)
+    assert P.ps_spec_verify_workspace_bytes(0, V) == 0
+    args = dict(target_probs=1 << 22, draft_probs=1 << 23, draft_tokens=1 << 24, draft_start=1 << 25,
+                accept_uniforms=1 << 26, sample_uniforms=1 << 27, num_seqs=S, total_drafts=128,
+                vocab_size=V, num_accepted=1 << 28, next_token=1 << 29, workspace=1 << 30,
+                workspace_bytes=ws)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        P.ps_spec_verify(**a)
+
+    _expect_error(INV, call, num_seqs=-1, match="num_seqs")
+    _expect_error(INV, call, total_drafts=-1, match="total_drafts")
+    _expect_error(UNS, call, vocab_size=0, match="vocab_size")
+    _expect_error(UNS, call, vocab_size=(1 << 23) + 1, match="vocab_size")
+    _expect_error(WS, call, workspace_bytes=ws - 1)
+    _expect_error(INV, call, workspace=(1 << 30) + 4, match="aligned")
+    _expect_error(INV, call, target_probs=0, match="NULL")
+    _expect_error(INV, call, draft_tokens=0, match="NULL")
+    # no drafts: the draft arrays may be NULL (the call is then plain sampling); zero sequences is a no-op
+    P.ps_spec_verify(0, 0, 0, 0, 0, 0, 0, 0, V, 0, 0, 0, 0)
+
+
 def test_split_plan_depends_only_on_logical_lengths():
     a = workloads.config(3, values=False)
     b = workloads.build_step("b", 77, "f16", 12, 2, 128, a.num_blocks, a.q_lens, a.num_computed,

@@ -242,3 +242,90 @@ def random_step(seed: int, dtype="f16", num_q_heads=12, num_kv_heads=2, head_dim
     return build_step(f"random-{seed}", seed, dtype, num_q_heads, num_kv_heads, head_dim,
                       num_blocks, q_lens.tolist(), num_computed.tolist(), rng=rng,
                       num_layers=num_layers, layer=layer, values=values)
+
+
+# --------------------------------------------------------------------------
+# Speculative verify rounds: the distributions a verify pass hands to the
+# rejection sampler. Input synthesis only (target and draft distributions,
+# draft tokens drawn by the proposer, uniforms); the acceptance test and
+# the residual / bonus draws are not here.
+
+QWEN25_VOCAB = 151936
+
+
+@dataclasses.dataclass
+class SpecRound:
+    """One batch of verify rounds (all host memory)."""
+    name: str
+    vocab: int
+    target_probs: np.ndarray   # float32 [total_drafts + S, V]: rows p_0..p_k of each sequence
+    draft_probs: np.ndarray    # float32 [total_drafts, V]: rows q_0..q_{k-1}
+    draft_tokens: np.ndarray   # int32 [total_drafts]
+    draft_start: np.ndarray    # int32 [S + 1], exclusive prefix sum of the draft counts
+    accept_u: np.ndarray       # float64 [total_drafts], uniforms in [0, 1)
+    sample_u: np.ndarray       # float64 [S]
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.draft_start) - 1
+
+    @property
+    def total_drafts(self) -> int:
+        return int(self.draft_start[-1])
+
+
+def _softmax_rows(z: np.ndarray) -> np.ndarray:
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def spec_round(name: str, seed: int, num_drafts: Sequence[int], vocab: int, logit_scale: float = 6.0,
+               draft_noise: float = 1.5, proposer: str = "draft", copy_rate: float = 0.9) -> SpecRound:
+    """Seeded verify rounds.
+
+    Recipe: one PCG64 generator; per sequence, in order: k + 1 target
+    logit rows z ~ N(0, logit_scale^2) (fp64), then the draft rows, then
+    the drafts. Target rows are softmax(z) rounded to fp32 (peaked like a
+    language model's next-token distribution: the top token typically
+    holds tens of percent). Proposer "draft" (a small draft model):
+    q_i = softmax(z_i + N(0, draft_noise^2)) and d_i is drawn from q_i.
+    Proposer "ngram" (prompt lookup, deterministic): q_i is one-hot at
+    d_i, which is the target's top token with probability copy_rate and
+    a uniform random token otherwise. Uniforms come last: one per draft,
+    then one per sequence.
+    """
+    rng = np.random.default_rng(seed)
+    ks = [int(k) for k in num_drafts]
+    S, total = len(ks), int(sum(ks))
+    tp = np.empty((total + S, vocab), np.float32)
+    dp = np.zeros((total, vocab), np.float32)
+    dt = np.empty(total, np.int32)
+    starts = np.zeros(S + 1, np.int32)
+    starts[1:] = np.cumsum(ks)
+    for s, k in enumerate(ks):
+        z = rng.standard_normal((k + 1, vocab)) * logit_scale
+        tp[starts[s] + s: starts[s] + s + k + 1] = _softmax_rows(z).astype(np.float32)
+        for i in range(k):
+            row = starts[s] + i
+            if proposer == "draft":
+                q = _softmax_rows(z[i] + rng.standard_normal(vocab) * draft_noise)
+                dp[row] = q.astype(np.float32)
+                c = np.cumsum(dp[row].astype(np.float64))
+                dt[row] = min(int(np.searchsorted(c, rng.random() * c[-1], side="right")), vocab - 1)
+            else:
+                top = int(np.argmax(z[i]))
+                dt[row] = top if rng.random() < copy_rate else int(rng.integers(0, vocab))
+                dp[row, dt[row]] = 1.0
+    au = rng.random(total)
+    su = rng.random(S)
+    return SpecRound(name, vocab, tp, dp, dt, starts, au, su)
+
+
+def spec_config(idx: int, proposer: str = "draft") -> SpecRound:
+    """The verify rows of named step ``idx``: every sequence scheduled with
+    1 + k tokens (k >= 1) is one round of k drafts over the Qwen2.5
+    vocabulary."""
+    st = config(idx, values=False)
+    ks = [int(n) - 1 for n in st.q_lens if 2 <= int(n) <= 9]
+    return spec_round(f"{st.name}-verify-{proposer}", 1000 + idx, ks, QWEN25_VOCAB, proposer=proposer)
