@@ -230,6 +230,26 @@ ps_status ps_paged_attention(const void *q, const ps_pool *pool,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The whole step in the fewest launches: ps_reshape_and_cache followed by
+ * ps_paged_attention, with the same arguments and results (pool contents
+ * and output bit for bit). When the plan puts every sequence on the
+ * decode / verify kernel, the scatter is fused into it: keys of this step
+ * are read from k and v directly, and the work item that holds a
+ * sequence's last keys writes them into their slots, so the step is one
+ * attention launch (plus the split-K merge) instead of two. Otherwise the
+ * scatter is launched first. Same checks and errors as the two calls.
+ *
+ *   k, v, slot_mapping  as for ps_reshape_and_cache
+ *   the rest            as for ps_paged_attention
+ */
+ps_status ps_step(const void *q, const void *k, const void *v, const int32_t *slot_mapping,
+                  const ps_pool *pool, const int32_t *block_tables, int32_t block_table_stride,
+                  const int32_t *query_start_loc, const int32_t *num_computed_tokens,
+                  const int32_t *context_lens, void *out, int32_t num_seqs, int32_t num_tokens,
+                  int32_t num_q_heads, float scale, const ps_plan *plan, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
  * Copy whole blocks between two pools of the same layout (num_layers,
  * block_size, num_kv_heads, head_dim, dtype; num_blocks may differ): for
  * every pair i and every layer, block src_blocks[i] of (src->k, src->v) is

@@ -10,5 +10,5 @@ from ._binding import (  # noqa: F401
     PsError, make_pool, ps_abi_version, ps_copy_blocks, ps_paged_attention, ps_plan_device_arrays,
     ps_plan_get_info, ps_plan_host_arrays, ps_plan_sizes, ps_plan_step, ps_plan_upload,
     ps_pool, ps_reshape_and_cache, ps_rope_reshape_and_cache, ps_spec_verify,
-    ps_spec_verify_workspace_bytes, status_string)
+    ps_spec_verify_workspace_bytes, ps_step, status_string)
 from .step import PackedStep  # noqa: F401

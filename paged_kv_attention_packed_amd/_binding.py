@@ -32,7 +32,7 @@ PS_PLAN_DEFAULT, PS_PLAN_ALL_DECODE, PS_PLAN_ALL_PREFILL = 0, 1, 2
 EXPORTED = [
     "ps_plan_step", "ps_plan_sizes", "ps_plan_upload", "ps_plan_device_arrays",
     "ps_plan_host_arrays", "ps_plan_get_info", "ps_plan_destroy", "ps_reshape_and_cache",
-    "ps_paged_attention", "ps_copy_blocks", "ps_rope_reshape_and_cache", "ps_spec_verify",
+    "ps_paged_attention", "ps_step", "ps_copy_blocks", "ps_rope_reshape_and_cache", "ps_spec_verify",
     "ps_spec_verify_workspace_bytes", "ps_status_string", "ps_last_error_message", "ps_abi_version",
 ]
 
@@ -100,6 +100,9 @@ lib.ps_paged_attention.restype = ctypes.c_int32
 lib.ps_paged_attention.argtypes = [_vp, ctypes.POINTER(ps_pool), _vp, ctypes.c_int32, _vp, _vp, _vp,
                                    _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_float, _vp, _vp, _sz, _vp]
+lib.ps_step.restype = ctypes.c_int32
+lib.ps_step.argtypes = [_vp, _vp, _vp, _vp, ctypes.POINTER(ps_pool), _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
+                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _vp, _vp, _sz, _vp]
 lib.ps_copy_blocks.restype = ctypes.c_int32
 lib.ps_copy_blocks.argtypes = [ctypes.POINTER(ps_pool), ctypes.POINTER(ps_pool), _vp, _vp, ctypes.c_int32, _vp]
 lib.ps_rope_reshape_and_cache.restype = ctypes.c_int32
@@ -239,6 +242,15 @@ def ps_paged_attention(q, pool: ps_pool, block_tables, block_table_stride: int, 
                                   _ptr(query_start_loc), _ptr(num_computed_tokens), _ptr(context_lens),
                                   _ptr(out), num_seqs, num_tokens, num_q_heads, scale, plan.handle,
                                   _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def ps_step(q, k, v, slot_mapping, pool: ps_pool, block_tables, block_table_stride: int, query_start_loc,
+            num_computed_tokens, context_lens, out, num_seqs: int, num_tokens: int, num_q_heads: int,
+            scale: float, plan: Plan, workspace, workspace_bytes: int, stream=None):
+    _check(lib.ps_step(_ptr(q), _ptr(k), _ptr(v), _ptr(slot_mapping), ctypes.byref(pool), _ptr(block_tables),
+                       block_table_stride, _ptr(query_start_loc), _ptr(num_computed_tokens),
+                       _ptr(context_lens), _ptr(out), num_seqs, num_tokens, num_q_heads, scale, plan.handle,
+                       _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def ps_copy_blocks(src: ps_pool, dst: ps_pool, src_blocks, dst_blocks, num_pairs: int, stream=None):

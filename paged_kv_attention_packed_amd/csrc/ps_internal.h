@@ -18,9 +18,13 @@ struct ps_item {
     int32_t key_begin;   // first key position (a multiple of 16)
     int32_t key_end;     // one past the last key position (<= context length)
     int32_t partial_row; // -1: write the output; else first workspace row of this item's partials
-    int32_t pad;
+    int32_t flags;       // PS_ITEM_* bits
 };
 static_assert(sizeof(ps_item) == 32, "ps_item layout");
+// The one item per (sequence, KV head) that holds the sequence's last keys
+// (last row range, last key slice): with the scatter fused into the
+// decode launch it writes the step's new K/V rows of its KV head.
+constexpr int32_t PS_ITEM_WRITES_NEW = 1;
 
 // A chunk of rows (at most ps_merge_rows(D)) of one set of split-K
 // partials, merged into the output by one workgroup of the merge kernel.
@@ -42,6 +46,7 @@ static_assert(sizeof(ps_merge) == 32, "ps_merge layout");
 constexpr int PS_BLOCK = 16;            // tokens per pool block
 constexpr int PS_DEC_TILE = 32;         // keys per decode-kernel wave iteration
 constexpr int PS_DEC_MAX_ROWS = 32;     // packed rows per decode work item (two 16-row MFMA tiles)
+constexpr int PS_DEC_MAX_SPLIT = 16384; // keys per decode work item at most
 constexpr int PS_PRE_TILE = 64;         // keys per prefill LDS tile
 constexpr int PS_PRE_WAVES = 4;         // waves per prefill work item
 constexpr int PS_PRE_ROWS_PER_WAVE = 32;
@@ -93,6 +98,15 @@ struct ps_attn_launch {
     int32_t decode_row_tiles;
     int32_t decode_waves;   // waves per decode workgroup (4, 8 or 16)
     float scale_log2;       // softmax scale * log2(e)
+    // Scatter fused into the decode kernel (steps without prefill items):
+    // keys at positions >= num_computed are read from k_new / v_new
+    // ([T, Hkv, D]) and the item holding a sequence's last keys writes
+    // them into their slots.
+    int32_t fuse_scatter;
+    int32_t num_slots;      // num_blocks * 16
+    const void *k_new;
+    const void *v_new;
+    const int32_t *slot_mapping;
 };
 
 // Rotary embedding + KV scatter launch (ps_rope.hip). The pair frequencies

@@ -250,6 +250,24 @@ __device__ inline void load_q_row(const ps_attn_launch &a, int r, int row_end, i
 }
 
 // ---------------------------------------------------------------------------
+// Waits. A bare s_barrier with explicit s_waitcnt: a fenced barrier would
+// also wait for global loads still in flight.
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// all waves reach this point with their LDS reads complete
+__device__ inline void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // KV scatter: one thread per 16 bytes of a token's K (and V) row.
 
 __global__ __launch_bounds__(256) void ps_scatter_kernel(const u32x4 *__restrict__ k,
@@ -326,6 +344,23 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
     const T *kp = static_cast<const T *>(a.pool_k) + a.layer_offset + (int64_t)j * D;
     const T *vp = static_cast<const T *>(a.pool_v) + a.layer_offset + (int64_t)j * D;
     const int kb = it.key_begin, ke = it.key_end;
+    // fused scatter: this step's keys (positions nc..) come from the inputs
+    const bool fused = a.fuse_scatter != 0;
+    const T *kn = fused ? static_cast<const T *>(a.k_new) + (int64_t)j * D + (int64_t)(qs0 - nc) * rs : kp;
+    const T *vn = fused ? static_cast<const T *>(a.v_new) + (int64_t)j * D + (int64_t)(qs0 - nc) * rs : vp;
+    const int new_lo = fused ? nc : INT32_MAX;   // keys in [new_lo, ke) are read from kn / vn
+
+    // The item's block ids go to LDS once: every tile after a wave's first
+    // reads its two ids there instead of waiting on a scalar load from the
+    // table. The staging loads are issued before the first tile's, so
+    // waiting for them does not wait for K/V.
+    __shared__ int32_t sbt[PS_DEC_MAX_SPLIT / PS_BLOCK];
+    constexpr int SPT = (PS_DEC_MAX_SPLIT / PS_BLOCK + 64 * NW - 1) / (64 * NW);
+    const int nb = (ke - kb + PS_BLOCK - 1) / PS_BLOCK;
+    const int32_t *btk = bt + (kb >> 4);
+    int32_t stg[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) stg[i] = btk[min(tid + i * 64 * NW, nb - 1)];
 
     u32x4 qf[RT][KU4];
     int lim[RT];
@@ -343,7 +378,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
         for (int t = 0; t < NT; ++t) o[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    constexpr bool DOUBLE_BUFFER = RT == 1;
+    // a second tile in flight does not fit the registers for fp32 rows of 128
+    constexpr bool DOUBLE_BUFFER = RT == 1 && !(ELT == 4 && D == 128);
     constexpr int NBUF = DOUBLE_BUFFER ? 2 : 1;
     u32x4 kf[NBUF][2][KU4];
     uint32_t vr[NBUF][8][VW];
@@ -352,16 +388,24 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
     // scalar loads (k0 is wave-uniform), so the vector loads never wait on
     // each other. Rows of an existing block past key_end are loaded (they
     // are in bounds) and zeroed or masked at use.
-    auto load_tile = [&](auto bufc, int k0) {
+    auto load_tile = [&](auto bufc, int k0, auto from_lds) {
         constexpr int buf = decltype(bufc)::value;
         const bool has1 = k0 + 16 < ke;
-        const int64_t blk0 = bt[k0 >> 4];
-        const int64_t blk1 = has1 ? (int64_t)bt[(k0 >> 4) + 1] : blk0;
+        int64_t blk0, blk1;
+        if constexpr (decltype(from_lds)::value) {
+            const int li = (k0 - kb) >> 4;
+            blk0 = __builtin_amdgcn_readfirstlane(sbt[li]);
+            blk1 = has1 ? __builtin_amdgcn_readfirstlane(sbt[li + 1]) : blk0;
+        } else {
+            blk0 = bt[k0 >> 4];
+            blk1 = has1 ? (int64_t)bt[(k0 >> 4) + 1] : blk0;
+        }
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int64_t blk = sb ? blk1 : blk0;
             if (sb == 0 || has1) {
-                const T *p = kp + (blk * 16 + c) * rs;
+                const int pos = k0 + sb * 16 + c;
+                const T *p = pos >= new_lo && pos < ke ? kn + (int64_t)pos * rs : kp + (blk * 16 + c) * rs;
 #pragma unroll
                 for (int u = 0; u < KU4; ++u)
                     kf[buf][sb][u] = *reinterpret_cast<const u32x4 *>(p + (u * 4 + q4) * (16 / ELT));
@@ -373,7 +417,10 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
             const int64_t blk = (jj >> 2) ? blk1 : blk0;
-            load_words<VW>(vp + (blk * 16 + 4 * q4 + (jj & 3)) * rs + EPL * c, vr[buf][jj]);
+            const int rw = 4 * q4 + (jj & 3);
+            const int pos = k0 + (jj >> 2) * 16 + rw;
+            const T *p = pos >= new_lo && pos < ke ? vn + (int64_t)pos * rs : vp + (blk * 16 + rw) * rs;
+            load_words<VW>(p + EPL * c, vr[buf][jj]);
         }
     };
 
@@ -429,30 +476,63 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
 
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
+    using FromTable = std::false_type;
+    using FromLds = std::true_type;
     const int ntiles = (ke - kb + PS_DEC_TILE - 1) / PS_DEC_TILE;
     int ti = wave;
+    // A wave's first tiles (one, or two with a second buffer) take their
+    // ids from the table; they are in flight while the staged ids are
+    // written. Waiting for the staging loads there waits for those tiles
+    // too, which costs little: they were issued together.
+    if (ti < ntiles) load_tile(B0{}, kb + ti * PS_DEC_TILE, FromTable{});
+    if constexpr (DOUBLE_BUFFER)
+        if (ti + NW < ntiles) load_tile(B1{}, kb + (ti + NW) * PS_DEC_TILE, FromTable{});
+#pragma unroll
+    for (int i = 0; i < SPT; ++i)
+        if (tid + i * 64 * NW < nb) sbt[tid + i * 64 * NW] = stg[i];
+    lds_barrier();
     if constexpr (!DOUBLE_BUFFER) {
         // two row tiles leave no registers for a second tile in flight;
         // the other resident waves cover the load latency
         for (; ti < ntiles; ti += NW) {
-            load_tile(B0{}, kb + ti * PS_DEC_TILE);
+            if (ti != wave) load_tile(B0{}, kb + ti * PS_DEC_TILE, FromLds{});
             compute_tile(B0{}, kb + ti * PS_DEC_TILE);
         }
     }
     if constexpr (DOUBLE_BUFFER) {
-        if (ti < ntiles) load_tile(B0{}, kb + ti * PS_DEC_TILE);
+        // tile ti + 2 NW streams into the buffer tile ti has just released
         while (ti < ntiles) {
-            if (ti + NW < ntiles) load_tile(B1{}, kb + (ti + NW) * PS_DEC_TILE);
             compute_tile(B0{}, kb + ti * PS_DEC_TILE);
+            if (ti + 2 * NW < ntiles) load_tile(B0{}, kb + (ti + 2 * NW) * PS_DEC_TILE, FromLds{});
             ti += NW;
             if (ti >= ntiles) break;
-            if (ti + NW < ntiles) load_tile(B0{}, kb + (ti + NW) * PS_DEC_TILE);
             compute_tile(B1{}, kb + ti * PS_DEC_TILE);
+            if (ti + 2 * NW < ntiles) load_tile(B1{}, kb + (ti + 2 * NW) * PS_DEC_TILE, FromLds{});
             ti += NW;
         }
     }
 
-    // ---- merge the 4 waves' states
+    // ---- fused scatter: the item holding the sequence's last keys (last
+    // row range, last key slice) copies this step's K/V rows of its KV
+    // head into their slots. No item of this launch reads those slots
+    // from the pool.
+    if (fused && (it.flags & PS_ITEM_WRITES_NEW)) {
+        constexpr int WPR = D * ELT / 16;   // 16-byte words per head row
+        const int n = ke - nc;
+        u32x4 *pk = reinterpret_cast<u32x4 *>(const_cast<T *>(kp));
+        u32x4 *pv = reinterpret_cast<u32x4 *>(const_cast<T *>(vp));
+        const int64_t rw = rs * ELT / 16;   // 16-byte words from one slot (or token) to the next
+        for (int w = tid; w < 2 * n * WPR; w += 64 * NW) {
+            const int which = w / (n * WPR), r2 = w - which * n * WPR;
+            const int i = r2 / WPR, cw = r2 - i * WPR;
+            const int32_t slot = a.slot_mapping[qs0 + i];
+            if ((uint32_t)slot >= (uint32_t)a.num_slots) continue;
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(which ? vn : kn) + (int64_t)(nc + i) * rw;
+            (which ? pv : pk)[(int64_t)slot * rw + cw] = src[cw];
+        }
+    }
+
+    // ---- merge the waves' states
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         l[rt] = xor_sum(l[rt]);
@@ -519,20 +599,6 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
 // reads bank-conflict free without padding (the DMA writes whole 1 KiB
 // lines). Hand-offs use a bare s_barrier with explicit s_waitcnt, since a
 // fenced barrier would also wait for the tile still in flight.
-
-template <int N>
-__device__ inline void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// all waves reach this point with their LDS reads complete
-__device__ inline void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 // one 16-byte global -> LDS DMA per lane; lane l lands at lds + 16 * l
 __device__ inline void dma16(const void *src, uint8_t *lds) {
@@ -623,6 +689,11 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
     const T *kp = static_cast<const T *>(a.pool_k) + a.layer_offset + (int64_t)j * D;
     const T *vp = static_cast<const T *>(a.pool_v) + a.layer_offset + (int64_t)j * D;
     const int kb = it.key_begin, ke = it.key_end;
+    // fused scatter: this step's keys (positions nc..) come from the inputs
+    const bool fused = a.fuse_scatter != 0;
+    const T *kn = fused ? static_cast<const T *>(a.k_new) + (int64_t)j * D + (int64_t)(qs0 - nc) * rs : kp;
+    const T *vn = fused ? static_cast<const T *>(a.v_new) + (int64_t)j * D + (int64_t)(qs0 - nc) * rs : vp;
+    const int new_lo = fused ? nc : INT32_MAX;   // keys in [new_lo, ke) are read from kn / vn
 
     const int wr0 = it.row_begin + wave * PS_PRE_ROWS_PER_WAVE;
     const bool active = wr0 < it.row_end;

@@ -186,9 +186,11 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                 else { pre_keys += kmax * Hkv; pre_tiles += Hkv; }
             }
         }
-        const int64_t dec_split = env_int(
-            "PS_DECODE_SPLIT",
-            std::min<int64_t>(16384, std::max<int64_t>(2048, round_up(ceil_div(dec_keys, 512), 128))));
+        const int64_t dec_split = std::min<int64_t>(
+            PS_DEC_MAX_SPLIT,
+            round_up(std::max<int64_t>(PS_BLOCK, env_int("PS_DECODE_SPLIT",
+                                                         std::max<int64_t>(2048, round_up(ceil_div(dec_keys, 512), 128)))),
+                     PS_BLOCK));
         const int64_t pre_split = env_int(
             "PS_PREFILL_SPLIT",
             // only long key ranges are worth splitting: the partials of a
@@ -221,6 +223,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                         it.key_begin = (int32_t)bounds[i];
                         it.key_end = (int32_t)bounds[i + 1];
                         it.partial_row = ns > 1 ? (int32_t)(base + i * (r1 - r0)) : -1;
+                        it.flags = r1 == rows && i == ns - 1 ? PS_ITEM_WRITES_NEW : 0;
                         (d ? dec : pre).push_back(it);
                     }
                     if (ns > 1) {
@@ -390,14 +393,15 @@ extern "C" void ps_plan_destroy(ps_plan *plan) { delete plan; }
 // ---------------------------------------------------------------------------
 // ps_paged_attention: argument checks against the plan, then the launches.
 
-extern "C" ps_status ps_paged_attention(const void *q, const ps_pool *pool,
-                                        const int32_t *block_tables, int32_t block_table_stride,
-                                        const int32_t *query_start_loc,
-                                        const int32_t *num_computed_tokens,
-                                        const int32_t *context_lens, void *out,
-                                        int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
-                                        float scale, const ps_plan *plan,
-                                        void *workspace, size_t workspace_bytes, void *stream) {
+// Argument checks against the plan and the launch record; *empty is set
+// for a step without tokens (nothing to launch).
+static ps_status prepare_attention(const void *q, const ps_pool *pool, const int32_t *block_tables,
+                                   int32_t block_table_stride, const int32_t *query_start_loc,
+                                   const int32_t *num_computed_tokens, const int32_t *context_lens,
+                                   void *out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                   float scale, const ps_plan *plan, void *workspace,
+                                   size_t workspace_bytes, ps_attn_launch &a, bool *empty) {
+    *empty = false;
     if (!plan) return ps_fail(PS_ERR_INVALID_ARGUMENT, "plan is NULL");
     if (!pool) return ps_fail(PS_ERR_INVALID_ARGUMENT, "pool is NULL");
     if (num_seqs != plan->S || num_tokens != plan->T || num_q_heads != plan->Hq)
@@ -422,12 +426,15 @@ extern "C" ps_status ps_paged_attention(const void *q, const ps_pool *pool,
     if (wl.bytes > 0 && (!workspace || ((uintptr_t)workspace & 255)))
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "workspace is NULL or not 256-byte aligned");
     if (!plan->dev) return ps_fail(PS_ERR_INVALID_ARGUMENT, "plan has not been uploaded");
-    if (num_tokens == 0) return PS_OK;
+    if (num_tokens == 0) {
+        *empty = true;
+        return PS_OK;
+    }
     if (!q || !out || !pool->k || !pool->v || !block_tables || !query_start_loc ||
         !num_computed_tokens || !context_lens)
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "a device pointer is NULL");
 
-    ps_attn_launch a{};
+    a = ps_attn_launch{};
     a.q = q;
     a.out = out;
     a.pool_k = pool->k;
@@ -457,10 +464,55 @@ extern "C" ps_status ps_paged_attention(const void *q, const ps_pool *pool,
     a.decode_row_tiles = plan->dec_rt;
     // few decode items: more waves per item, so a short slice is read in
     // one round trip; many items: 4 waves each fill the chip
-    a.decode_waves = (int32_t)env_int("PS_DECODE_WAVES",
-                                      plan->n_dec < 512 ? (plan->D == 64 ? 16 : 8) : 4);
+    a.decode_waves = (int32_t)env_int("PS_DECODE_WAVES", plan->n_dec < 512 ? 8 : 4);
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.num_slots = plan->num_blocks * PS_BLOCK;
+    return PS_OK;
+}
+
+extern "C" ps_status ps_paged_attention(const void *q, const ps_pool *pool,
+                                        const int32_t *block_tables, int32_t block_table_stride,
+                                        const int32_t *query_start_loc,
+                                        const int32_t *num_computed_tokens,
+                                        const int32_t *context_lens, void *out,
+                                        int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                        float scale, const ps_plan *plan,
+                                        void *workspace, size_t workspace_bytes, void *stream) {
+    ps_attn_launch a;
+    bool empty;
+    const ps_status st = prepare_attention(q, pool, block_tables, block_table_stride, query_start_loc,
+                                           num_computed_tokens, context_lens, out, num_seqs, num_tokens,
+                                           num_q_heads, scale, plan, workspace, workspace_bytes, a, &empty);
+    if (st != PS_OK || empty) return st;
     const int err = ps_launch_attention(a, stream);
     if (err != 0) return ps_fail(PS_ERR_HIP, "attention launch: %s", ps_hip_error_string(err));
+    return PS_OK;
+}
+
+extern "C" ps_status ps_step(const void *q, const void *k, const void *v, const int32_t *slot_mapping,
+                             const ps_pool *pool, const int32_t *block_tables, int32_t block_table_stride,
+                             const int32_t *query_start_loc, const int32_t *num_computed_tokens,
+                             const int32_t *context_lens, void *out, int32_t num_seqs, int32_t num_tokens,
+                             int32_t num_q_heads, float scale, const ps_plan *plan, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    ps_attn_launch a;
+    bool empty;
+    ps_status st = prepare_attention(q, pool, block_tables, block_table_stride, query_start_loc,
+                                     num_computed_tokens, context_lens, out, num_seqs, num_tokens,
+                                     num_q_heads, scale, plan, workspace, workspace_bytes, a, &empty);
+    if (st != PS_OK || empty) return st;
+    if (!k || !v || !slot_mapping) return ps_fail(PS_ERR_INVALID_ARGUMENT, "k, v or slot_mapping is NULL");
+    if (plan->n_pre == 0 && plan->n_dec > 0) {
+        // every sequence on the decode kernel: the scatter rides along
+        a.fuse_scatter = 1;
+        a.k_new = k;
+        a.v_new = v;
+        a.slot_mapping = slot_mapping;
+    } else {
+        st = ps_reshape_and_cache(k, v, slot_mapping, num_tokens, pool, stream);
+        if (st != PS_OK) return st;
+    }
+    const int err = ps_launch_attention(a, stream);
+    if (err != 0) return ps_fail(PS_ERR_HIP, "step launch: %s", ps_hip_error_string(err));
     return PS_OK;
 }

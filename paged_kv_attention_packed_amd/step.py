@@ -41,12 +41,23 @@ class PackedStep:
                              self.num_tokens, self.num_q_heads, scale, self.plan, self.ws,
                              self.ws_bytes, stream)
 
-    def run(self, q, k, v, pool: B.ps_pool, out, scale: float, stream=None, rope_theta=None):
-        """The whole step: scatter this step's K/V, then attend. With
-        ``rope_theta`` q and k arrive unrotated: q is rotated in place and k
-        on its way into the pool."""
-        if rope_theta is None:
-            self.reshape_and_cache(k, v, pool, stream)
-        else:
+    def step(self, q, k, v, pool: B.ps_pool, out, scale: float, stream=None):
+        """Scatter and attention through ps_step (fused when the plan allows)."""
+        a = self.arrays
+        B.ps_step(q, k, v, a.slot_mapping, pool, a.block_tables, a.block_table_stride, a.query_start_loc,
+                  a.num_computed_tokens, a.context_lens, out, self.num_seqs, self.num_tokens,
+                  self.num_q_heads, scale, self.plan, self.ws, self.ws_bytes, stream)
+
+    def run(self, q, k, v, pool: B.ps_pool, out, scale: float, stream=None, rope_theta=None,
+            separate=False):
+        """The whole step: scatter this step's K/V, then attend (ps_step, or
+        the two calls with ``separate``). With ``rope_theta`` q and k arrive
+        unrotated: q is rotated in place and k on its way into the pool."""
+        if rope_theta is not None:
             self.rope_reshape_and_cache(q, q, k, v, pool, rope_theta, stream)
-        self.attention(q, pool, out, scale, stream)
+            self.attention(q, pool, out, scale, stream)
+        elif separate:
+            self.reshape_and_cache(k, v, pool, stream)
+            self.attention(q, pool, out, scale, stream)
+        else:
+            self.step(q, k, v, pool, out, scale, stream)

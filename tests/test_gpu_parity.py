@@ -33,8 +33,9 @@ def _to_dev_pool(arr, dtype):
     return torch.from_numpy(arr).to(DEV).view(dtype)
 
 
-def run_on_gpu(st, flags=P.PS_PLAN_DEFAULT, pools=None, repeat=1):
-    """Run the step through the library; returns (out, pool_k, pool_v) on the host."""
+def run_on_gpu(st, flags=P.PS_PLAN_DEFAULT, pools=None, repeat=1, separate=False):
+    """Run the step through the library (ps_step, or the two calls with
+    ``separate``); returns (out, pool_k, pool_v) on the host."""
     pk, pv = pools if pools is not None else H.host_pools(st)
     gk = _to_dev_pool(pk, st.dtype)
     gv = _to_dev_pool(pv, st.dtype)
@@ -43,7 +44,7 @@ def run_on_gpu(st, flags=P.PS_PLAN_DEFAULT, pools=None, repeat=1):
     q, k, v = st.q.to(DEV), st.k.to(DEV), st.v.to(DEV)
     out = torch.full_like(q, float("nan"))
     stream = torch.cuda.current_stream()
-    step.run(q, k, v, pool, out, st.scale, stream)
+    step.run(q, k, v, pool, out, st.scale, stream, separate=separate)
     for _ in range(repeat - 1):
         step.attention(q, pool, out, st.scale, stream)
     torch.cuda.synchronize()
@@ -229,3 +230,38 @@ def test_forced_splits_merge_exactly(split, monkeypatch):
             _note(f"split={split} flags={flags} {dt} q_lens={st.q_lens.tolist()}")
             out, _, _ = run_on_gpu(st, flags=flags)
             check_out(st, out)
+
+
+def _same_as_separate_calls(st, flags):
+    pools = H.host_pools(st)
+    out_f, gk_f, gv_f = run_on_gpu(st, flags=flags, pools=pools)
+    out_s, gk_s, gv_s = run_on_gpu(st, flags=flags, pools=pools, separate=True)
+    assert np.array_equal(H.bits(out_f), H.bits(out_s)), "ps_step output differs from the two calls"
+    assert np.array_equal(gk_f, gk_s) and np.array_equal(gv_f, gv_s), "ps_step pool differs"
+    check_pool(st, pools, gk_f, gv_f)
+    return out_f
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_step_entry_matches_separate_calls(idx):
+    # ps_step fuses the scatter into the decode launch when no sequence
+    # takes the prefill kernel (configs 2 and 4, and 1 and 3 when forced
+    # onto the decode kernel); results must be the two calls' bit for bit
+    st = workloads.config(idx)
+    for flags in (P.PS_PLAN_DEFAULT, P.PS_PLAN_ALL_DECODE):
+        _note(f"config {idx} step entry flags={flags}")
+        _same_as_separate_calls(st, flags)
+
+
+@pytest.mark.parametrize("split", [16, 64])
+def test_step_entry_fused_with_splits_and_row_ranges(split, monkeypatch):
+    # split key slices (only the item holding a sequence's last keys writes
+    # them) and, forced onto the decode kernel, sequences with several row
+    # ranges per KV head
+    monkeypatch.setenv("PS_DECODE_SPLIT", str(split))
+    for dt, hq, hkv, d in (("bf16", 12, 2, 128), ("f16", 14, 2, 64), ("f32", 4, 2, 64), ("f32", 4, 1, 128)):
+        st = workloads.random_step(500 + split + hq + d, dtype=dt, num_q_heads=hq, num_kv_heads=hkv,
+                                   head_dim=d, num_seqs=7, max_q=40, max_ctx=500)
+        _note(f"fused split={split} {dt} D={d} q_lens={st.q_lens.tolist()}")
+        out = _same_as_separate_calls(st, P.PS_PLAN_ALL_DECODE)
+        check_out(st, out)
