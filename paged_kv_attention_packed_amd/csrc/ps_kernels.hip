@@ -689,11 +689,6 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
     const T *kp = static_cast<const T *>(a.pool_k) + a.layer_offset + (int64_t)j * D;
     const T *vp = static_cast<const T *>(a.pool_v) + a.layer_offset + (int64_t)j * D;
     const int kb = it.key_begin, ke = it.key_end;
-    // fused scatter: this step's keys (positions nc..) come from the inputs
-    const bool fused = a.fuse_scatter != 0;
-    const T *kn = fused ? static_cast<const T *>(a.k_new) + (int64_t)j * D + (int64_t)(qs0 - nc) * rs : kp;
-    const T *vn = fused ? static_cast<const T *>(a.v_new) + (int64_t)j * D + (int64_t)(qs0 - nc) * rs : vp;
-    const int new_lo = fused ? nc : INT32_MAX;   // keys in [new_lo, ke) are read from kn / vn
 
     const int wr0 = it.row_begin + wave * PS_PRE_ROWS_PER_WAVE;
     const bool active = wr0 < it.row_end;
