@@ -62,14 +62,16 @@ __device__ inline float cvt_out(float x, TF32) { return x; }
 __device__ inline _Float16 cvt_out(float x, TF16) { return (_Float16)x; }
 __device__ inline __bf16 cvt_out(float x, TBF16) { return (__bf16)x; }
 
-// two fp32 -> packed pair of 16-bit values (low half = first)
+// two fp32 -> packed pair of 16-bit values (low half = first), round to
+// nearest even: one v_cvt_pk_{f16,bf16}_f32
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ inline uint32_t pack2(float x, float y, TF16) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, f16x2));
 }
 __device__ inline uint32_t pack2(float x, float y, TBF16) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
 }
 
 __device__ inline f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c, TF16) {
@@ -601,11 +603,22 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
 // fenced barrier would also wait for the tile still in flight.
 
 // one 16-byte global -> LDS DMA per lane; lane l lands at lds + 16 * l
+// Issued as inline asm: the compiler cannot tell which LDS bytes a DMA in
+// flight will write, so for the builtin (or an asm that clobbers memory) it
+// waits for every DMA in flight, the next tiles' too, before each LDS read.
+// Ordering is explicit instead: wait_vmcnt for this thread's DMAs, then
+// lds_barrier (whose asm does clobber memory) for everyone's. m0 holds the
+// LDS destination; nothing else on gfx950 reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is a reserved register: the clobber is the point
 __device__ inline void dma16(const void *src, uint8_t *lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+    const uint32_t off = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(off) : "m0");
 #endif
 }
+#pragma clang diagnostic pop
 
 // 16-byte chunk position of `chunk` in key row `row`: XOR-swizzled so that
 // 16 consecutive lanes reading one chunk of 16 consecutive rows, or 16
@@ -656,7 +669,7 @@ __device__ inline void lds_row_words(const uint8_t *rowp, int row, int off, uint
 
 // TK: keys per tile; OCC: waves per SIMD the register budget is sized for
 // (1: 512 registers, accumulators may live in AGPRs; 2: 256 registers)
-template <class DT, int D, int TK, int OCC>
+template <class DT, int D, int TK, int OCC, int NST>
 __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_launch a) {
     using G = Geo<DT, D>;
     using T = typename DT::T;
@@ -671,10 +684,16 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
     static_assert(CPR >= 8 && TILEB % 4096 == 0, "tile geometry");
     static_assert(2 * PS_PRE_ROWS_PER_WAVE * D * ELT <= STAGEB, "output staging fits the ring");
 
-    // the two ring stages are separate objects so the compiler can tell a
-    // read of one from the DMA still filling the other
+    // the ring stages are separate objects so the compiler can tell a read
+    // of one from the DMA still filling another
+    static_assert(NST == 2 || NST == 3, "ring stages");
     __shared__ __attribute__((aligned(1024))) uint8_t ring0[STAGEB];
     __shared__ __attribute__((aligned(1024))) uint8_t ring1[STAGEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring2[NST == 3 ? STAGEB : 1024];
+    auto stage = [&](auto sc) -> uint8_t * {
+        constexpr int st = decltype(sc)::value;
+        return st == 0 ? ring0 : st == 1 ? ring1 : ring2;
+    };
     __shared__ int32_t sbt[PS_PRE_MAX_KEYS / PS_BLOCK];  // the item's block ids
 
     const ps_item it = a.prefill_items[blockIdx.x];
@@ -727,7 +746,7 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
     const int trow = tid / CPR;        // this thread's row within such a group
     const int tpos = tid % CPR;        // and its 16-byte position in that row
     auto issue_tile = [&](auto stagec, int k0) {
-        uint8_t *const ring = decltype(stagec)::value ? ring1 : ring0;
+        uint8_t *const ring = stage(stagec);
         int64_t blk[NSB];
         const int b0 = (k0 - kb) >> 4;
         blk[0] = __builtin_amdgcn_readfirstlane(sbt[b0]);
@@ -748,7 +767,7 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
     };
 
     auto compute_tile = [&](auto stagec, int k0) {
-        const uint8_t *ksm = decltype(stagec)::value ? ring1 : ring0;
+        const uint8_t *ksm = stage(stagec);
         const uint8_t *vsm = ksm + TILEB;
         const bool full = (k0 + TK <= ke) && (k0 + TK - 1 <= lim_lo);
         f32x4 sacc[RT][NSB];
@@ -762,15 +781,23 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
             for (int rt = 0; rt < RT; ++rt) sacc[rt][sb] = qk_tile<DT, D>(kf, qf[rt]);
         }
         float pv[RT][4 * NSB];
+        if (full) {  // (wave-uniform) every key of the tile is visible to every row
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            // key k0 + sb*16 + 4*q4 + i is visible iff sb*16 + i <= vis
-            const int vis = min(ke - 1, lim[rt]) - k0 - 4 * q4;
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int sb = 0; sb < NSB; ++sb)
+                for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    pv[rt][sb * 4 + i] = (full || sb * 16 + i <= vis) ? sacc[rt][sb][i] : kNegInf;
+                    for (int i = 0; i < 4; ++i) pv[rt][sb * 4 + i] = sacc[rt][sb][i];
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                // key k0 + sb*16 + 4*q4 + i is visible iff sb*16 + i <= vis
+                const int vis = min(ke - 1, lim[rt]) - k0 - 4 * q4;
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pv[rt][sb * 4 + i] = sb * 16 + i <= vis ? sacc[rt][sb][i] : kNegInf;
+            }
         }
         softmax_update(pv, a.scale_log2, m, l, o);
         // P.V over 32-key halves
@@ -782,9 +809,9 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
             const int j16 = lane & 15;
             const int trow = 4 * q4 + (j16 >> 2);
             const int tbyte = (j16 & 3) * 8;  // within a 32-byte d tile
+            // (V rows past key_end were zeroed in LDS before this tile)
 #pragma unroll
             for (int h = 0; h < NSB / 2; ++h) {
-                const bool ragged = k0 + TK > ke;
                 u32x4 pb[RT];
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
@@ -793,27 +820,11 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
                         pb[rt][e] = pack2(pv[rt][8 * h + 2 * e], pv[rt][8 * h + 2 * e + 1], DT{});
                 const int r0 = 32 * h + trow, r1 = r0 + 16;
                 const uint8_t *v0 = vsm + r0 * ROWB, *v1 = vsm + r1 * ROWB;
-                // rows past key_end hold whatever the pool had: zero them.
-                // Element e of this lane's lo / hi words came from row
-                // 32h + 4q4 + e (+ 16 for hi).
-                u32x2 mlo = {~0u, ~0u}, mhi = {~0u, ~0u};
-                if (ragged) {
-                    const int vl = ke - k0 - 32 * h - 4 * q4;
-#pragma unroll
-                    for (int w = 0; w < 2; ++w) {
-                        mlo[w] = (2 * w < vl ? 0xFFFFu : 0u) | (2 * w + 1 < vl ? 0xFFFF0000u : 0u);
-                        mhi[w] = (16 + 2 * w < vl ? 0xFFFFu : 0u) | (17 + 2 * w < vl ? 0xFFFF0000u : 0u);
-                    }
-                }
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     const int b = t * 32 + tbyte;
-                    u32x2 lo = lds_read_tr16(v0 + swz<ROWB>(b >> 4, r0) * 16 + (b & 15));
-                    u32x2 hi = lds_read_tr16(v1 + swz<ROWB>(b >> 4, r1) * 16 + (b & 15));
-                    if (ragged) {
-                        lo &= mlo;
-                        hi &= mhi;
-                    }
+                    const u32x2 lo = lds_read_tr16(v0 + swz<ROWB>(b >> 4, r0) * 16 + (b & 15));
+                    const u32x2 hi = lds_read_tr16(v1 + swz<ROWB>(b >> 4, r1) * 16 + (b & 15));
                     const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) o[rt][t] = mfma32(av, pb[rt], o[rt][t], DT{});
@@ -862,24 +873,48 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
 
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    // tile ti sits in stage ti & 1; tile ti + 1 streams into the other
-    // stage while ti is consumed
-    // The last step re-reads its own tile into the idle stage instead of
-    // branching around the issue: a branch here would make the compiler
-    // wait for the in-flight tile before every LDS read.
-    auto step = [&](auto cur, auto nxt, int ti, int ntiles) {
+    using S2 = std::integral_constant<int, 2>;
+    // Tile ti sits in stage ti % NST; the NST - 1 tiles after it stream in
+    // while it is consumed. One barrier per tile: once every thread's
+    // loads of tile ti have landed, every wave has also finished tile
+    // ti - 1, so its stage takes tile ti + NST - 1.
+    // Past the end a step re-reads its own tile instead of branching around
+    // the issue: a branch here would make the compiler wait for the tiles
+    // in flight before every LDS read.
+    auto step = [&](auto cur, auto ahead, int ti, int ntiles) {
         const int k0 = kb + ti * TK;
-        issue_tile(nxt, ti + 1 < ntiles ? k0 + TK : k0);
-        wait_vmcnt<NLD>();  // this thread's loads of tile ti have landed
-        lds_barrier();      // ... and every other thread's
+        wait_vmcnt<(NST - 2) * NLD>();  // this thread's loads of tile ti have landed
+        lds_barrier();                  // ... and every other thread's
+        issue_tile(ahead, ti + NST - 1 < ntiles ? k0 + (NST - 1) * TK : k0);
+        if constexpr (ELT == 2) {
+            // The last tile of the slice: V rows past key_end hold whatever
+            // the pool had (even NaN), and a zero weight would not cancel
+            // them. Zero them in LDS (whole rows: the swizzle stays inside
+            // a row), so the P.V loop needs no masks.
+            if (k0 + TK > ke) {
+                uint8_t *vz = stage(cur) + TILEB;
+                const int first = ke - k0;
+                for (int x = tid; x < (TK - first) * CPR; x += 256)
+                    reinterpret_cast<u32x4 *>(vz + (first + x / CPR) * ROWB)[x % CPR] = u32x4{0u, 0u, 0u, 0u};
+                lds_barrier();
+            }
+        }
         if (active && k0 <= lim_hi) compute_tile(cur, k0);
-        lds_barrier();  // stage `cur` is free for tile ti + 2
     };
     const int ntiles = (ke - kb + TK - 1) / TK;
-    if (ntiles > 0) issue_tile(S0{}, kb);
-    for (int ti = 0; ti < ntiles; ti += 2) {
-        step(S0{}, S1{}, ti, ntiles);
-        if (ti + 1 < ntiles) step(S1{}, S0{}, ti + 1, ntiles);
+    if (ntiles > 0) {
+        issue_tile(S0{}, kb);
+        if constexpr (NST == 3) issue_tile(S1{}, ntiles > 1 ? kb + TK : kb);
+    }
+    for (int ti = 0; ti < ntiles; ti += NST) {
+        if constexpr (NST == 2) {
+            step(S0{}, S1{}, ti, ntiles);
+            if (ti + 1 < ntiles) step(S1{}, S0{}, ti + 1, ntiles);
+        } else {
+            step(S0{}, S2{}, ti, ntiles);
+            if (ti + 1 < ntiles) step(S1{}, S0{}, ti + 1, ntiles);
+            if (ti + 2 < ntiles) step(S2{}, S1{}, ti + 2, ntiles);
+        }
     }
 
     wait_vmcnt<0>();  // the last, unused tile must land before the ring is reused
@@ -978,9 +1013,10 @@ __global__ __launch_bounds__(256) void ps_merge_kernel(const ps_attn_launch a) {
 // Launchers
 
 // Prefill kernel shape (tuning knob, PS_PREFILL_VARIANT): 0 = 64-key tiles
-// (32 for fp32) at two waves per SIMD (default), 1 = the same tiles with a
-// 512-register budget at one wave per SIMD, 2 = 32-key tiles at two waves
-// per SIMD.
+// in a two-stage ring at two waves per SIMD (default for 16-bit data);
+// 1 = 32-key tiles in a three-stage ring; 2 = 32-key tiles in a two-stage
+// ring; 3 = 64-key tiles with a 512-register budget at one wave per SIMD.
+// fp32 rows always take 32-key tiles in two stages.
 int prefill_variant() {
     static const int v = [] {
         const char *e = std::getenv("PS_PREFILL_VARIANT");
@@ -1004,19 +1040,23 @@ hipError_t launch_attention_t(const ps_attn_launch &a, hipStream_t st) {
         }
     }
     if (a.n_prefill > 0) {
-        constexpr int TK = DT::ELT == 2 ? PS_PRE_TILE : PS_PRE_TILE / 2;
-        switch (prefill_variant()) {
-            case 1:
-                hipLaunchKernelGGL((ps_prefill_kernel<DT, D, TK, 1>), dim3(a.n_prefill), dim3(256), 0, st, a);
-                break;
-            case 2:
-                if constexpr (TK != 32) {  // (for fp32 this is the default shape)
-                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, 32, 2>), dim3(a.n_prefill), dim3(256), 0, st, a);
+        const dim3 grid(a.n_prefill), block(256);
+        if constexpr (DT::ELT == 4) {
+            hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 2>), grid, block, 0, st, a);
+        } else {
+            switch (prefill_variant()) {
+                case 1:
+                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 3>), grid, block, 0, st, a);
                     break;
-                }
-                [[fallthrough]];
-            default:
-                hipLaunchKernelGGL((ps_prefill_kernel<DT, D, TK, 2>), dim3(a.n_prefill), dim3(256), 0, st, a);
+                case 2:
+                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 2>), grid, block, 0, st, a);
+                    break;
+                case 3:
+                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE, 1, 2>), grid, block, 0, st, a);
+                    break;
+                default:
+                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE, 2, 2>), grid, block, 0, st, a);
+            }
         }
     }
     if (a.n_merge > 0)
