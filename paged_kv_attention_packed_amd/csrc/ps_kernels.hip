@@ -193,7 +193,9 @@ __device__ inline u32x4 v_operand(const uint32_t (&vr)[8][VW], int t) {
 // decision, so the rescale is a single uniform branch.
 constexpr float kLazyRescale = 8.f;
 
-template <int RT, int NS, int NT>
+// SUM = false: the caller accumulates the row sums itself (the prefill
+// kernel does it on MFMA, as an extra all-ones column tile of o).
+template <int RT, int NS, int NT, bool SUM = true>
 __device__ inline void softmax_update(float (&sv)[RT][NS], float c, float (&m)[RT], float (&l)[RT],
                                       f32x4 (&o)[RT][NT]) {
     float tmax[RT];
@@ -224,9 +226,9 @@ __device__ inline void softmax_update(float (&sv)[RT][NS], float c, float (&m)[R
 #pragma unroll
         for (int e = 0; e < NS; ++e) {
             sv[rt][e] = fast_exp2(__builtin_fmaf(sv[rt][e], c, -muse));
-            psum += sv[rt][e];
+            if constexpr (SUM) psum += sv[rt][e];
         }
-        l[rt] += psum;
+        if constexpr (SUM) l[rt] += psum;
     }
 }
 
@@ -618,6 +620,12 @@ __device__ inline void dma16(const void *src, uint8_t *lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(off) : "m0");
 #endif
 }
+// Same, addressed as a scalar base plus a 32-bit per-lane byte offset.
+__device__ inline void dma16_sv(const void *base, uint32_t voff, uint32_t lds_off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_off) : "m0");
+#endif
+}
 #pragma clang diagnostic pop
 
 // 16-byte chunk position of `chunk` in key row `row`: XOR-swizzled so that
@@ -728,14 +736,18 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
     wait_vmcnt<0>();
     __syncthreads();
 
+    // 16-bit data: o carries one more tile, the row sums of P, formed on
+    // MFMA against an all-ones V tile (rescaled with o, and summed over the
+    // same rounded P as the numerator)
+    constexpr int NTL = ELT == 2 ? NT + 1 : NT;
     float m[RT], l[RT];
-    f32x4 o[RT][NT];
+    f32x4 o[RT][NTL];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         m[rt] = kNegInf;
         l[rt] = 0.f;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) o[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NTL; ++t) o[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     // DMA the K/V tile of keys [k0, k0 + TK) into ring stage `stage`. Block
@@ -761,8 +773,12 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
             int64_t b = blk[r0 >> 4];
             if constexpr (RPI == 32) b = (trow >> 4) ? blk[(r0 >> 4) + 1] : b;
             const int inblk = (key & 15) * (int)rs + swz<ROWB>(tpos, key) * (16 / ELT);
-            const T *src = (kv ? vp : kp) + b * 16 * rs + inblk;
-            dma16(src, ring + i * 4096 + wave * 1024);
+            if constexpr (RPI == 32) {  // one instruction spans two blocks: per-lane address
+                dma16((kv ? vp : kp) + b * 16 * rs + inblk, ring + i * 4096 + wave * 1024);
+            } else {  // scalar block base, loop-invariant lane offset, scalar LDS slot
+                const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring;
+                dma16_sv((kv ? vp : kp) + b * 16 * rs, (uint32_t)inblk * ELT, lds0 + i * 4096 + wave * 1024);
+            }
         }
     };
 
@@ -799,7 +815,7 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
                     for (int i = 0; i < 4; ++i) pv[rt][sb * 4 + i] = sb * 16 + i <= vis ? sacc[rt][sb][i] : kNegInf;
             }
         }
-        softmax_update(pv, a.scale_log2, m, l, o);
+        softmax_update<RT, 4 * NSB, NTL, ELT != 2>(pv, a.scale_log2, m, l, o);
         // P.V over 32-key halves
         if constexpr (ELT == 2) {
             // A operand of O^T tile t straight from LDS with transposing
@@ -829,6 +845,10 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) o[rt][t] = mfma32(av, pb[rt], o[rt][t], DT{});
                 }
+                constexpr uint32_t one2 = std::is_same<DT, TBF16>::value ? 0x3F803F80u : 0x3C003C00u;
+                const u32x4 ones = {one2, one2, one2, one2};
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) o[rt][NTL - 1] = mfma32(ones, pb[rt], o[rt][NTL - 1], DT{});
             }
             return;
         }
@@ -920,7 +940,10 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
     wait_vmcnt<0>();  // the last, unused tile must land before the ring is reused
     __syncthreads();
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) l[rt] = xor_sum(l[rt]);
+    for (int rt = 0; rt < RT; ++rt) {
+        if constexpr (ELT == 2) l[rt] = o[rt][NTL - 1][0];  // every entry holds the row's sum
+        else l[rt] = xor_sum(l[rt]);
+    }
 
     if (it.partial_row >= 0) {
         if (!active) return;
