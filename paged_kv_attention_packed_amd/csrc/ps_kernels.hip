@@ -483,14 +483,23 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
     using FromTable = std::false_type;
     using FromLds = std::true_type;
     const int ntiles = (ke - kb + PS_DEC_TILE - 1) / PS_DEC_TILE;
+    // Items start their walk over the key range at different tiles, so that
+    // items sharing prefix blocks do not all ask for the same lines at once
+    // (softmax order is free; the order is a fixed function of the item).
+    const int rot = ntiles > 1 ? (int)((blockIdx.x * 13u) % (unsigned)ntiles) : 0;
+    auto key0 = [&](int t) {
+        int u = t + rot;
+        u -= u >= ntiles ? ntiles : 0;
+        return kb + u * PS_DEC_TILE;
+    };
     int ti = wave;
     // A wave's first tiles (one, or two with a second buffer) take their
     // ids from the table; they are in flight while the staged ids are
     // written. Waiting for the staging loads there waits for those tiles
     // too, which costs little: they were issued together.
-    if (ti < ntiles) load_tile(B0{}, kb + ti * PS_DEC_TILE, FromTable{});
+    if (ti < ntiles) load_tile(B0{}, key0(ti), FromTable{});
     if constexpr (DOUBLE_BUFFER)
-        if (ti + NW < ntiles) load_tile(B1{}, kb + (ti + NW) * PS_DEC_TILE, FromTable{});
+        if (ti + NW < ntiles) load_tile(B1{}, key0(ti + NW), FromTable{});
 #pragma unroll
     for (int i = 0; i < SPT; ++i)
         if (tid + i * 64 * NW < nb) sbt[tid + i * 64 * NW] = stg[i];
@@ -499,19 +508,19 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
         // two row tiles leave no registers for a second tile in flight;
         // the other resident waves cover the load latency
         for (; ti < ntiles; ti += NW) {
-            if (ti != wave) load_tile(B0{}, kb + ti * PS_DEC_TILE, FromLds{});
-            compute_tile(B0{}, kb + ti * PS_DEC_TILE);
+            if (ti != wave) load_tile(B0{}, key0(ti), FromLds{});
+            compute_tile(B0{}, key0(ti));
         }
     }
     if constexpr (DOUBLE_BUFFER) {
         // tile ti + 2 NW streams into the buffer tile ti has just released
         while (ti < ntiles) {
-            compute_tile(B0{}, kb + ti * PS_DEC_TILE);
-            if (ti + 2 * NW < ntiles) load_tile(B0{}, kb + (ti + 2 * NW) * PS_DEC_TILE, FromLds{});
+            compute_tile(B0{}, key0(ti));
+            if (ti + 2 * NW < ntiles) load_tile(B0{}, key0(ti + 2 * NW), FromLds{});
             ti += NW;
             if (ti >= ntiles) break;
-            compute_tile(B1{}, kb + ti * PS_DEC_TILE);
-            if (ti + 2 * NW < ntiles) load_tile(B1{}, kb + (ti + 2 * NW) * PS_DEC_TILE, FromLds{});
+            compute_tile(B1{}, key0(ti));
+            if (ti + 2 * NW < ntiles) load_tile(B1{}, key0(ti + 2 * NW), FromLds{});
             ti += NW;
         }
     }
