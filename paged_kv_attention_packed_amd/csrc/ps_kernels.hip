@@ -686,12 +686,12 @@ __device__ inline void lds_row_words(const uint8_t *rowp, int row, int off, uint
 
 // TK: keys per tile; OCC: waves per SIMD the register budget is sized for
 // (1: 512 registers, accumulators may live in AGPRs; 2: 256 registers)
-template <class DT, int D, int TK, int OCC, int NST>
+template <class DT, int D, int TK, int OCC, int NST, int RPW>
 __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_launch a) {
     using G = Geo<DT, D>;
     using T = typename DT::T;
     constexpr int ELT = G::ELT, KU4 = G::KU4, VW = G::VW, NT = G::NT, EPL = G::EPL;
-    constexpr int RT = PS_PRE_ROWS_PER_WAVE / 16;
+    constexpr int RT = RPW / 16;  // 16-row MFMA tiles per wave
     constexpr int NSB = TK / 16;
     constexpr int ROWB = D * ELT;          // LDS bytes per key row
     constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
     constexpr int STAGEB = 2 * TILEB;      // K then V
     constexpr int NLD = STAGEB / 4096;     // 16-byte DMA loads per thread per stage
     static_assert(CPR >= 8 && TILEB % 4096 == 0, "tile geometry");
-    static_assert(2 * PS_PRE_ROWS_PER_WAVE * D * ELT <= STAGEB, "output staging fits the ring");
+    static_assert(2 * RPW * D * ELT <= STAGEB, "output staging fits the ring");
 
     // the ring stages are separate objects so the compiler can tell a read
     // of one from the DMA still filling another
@@ -726,9 +726,9 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
     const T *vp = static_cast<const T *>(a.pool_v) + a.layer_offset + (int64_t)j * D;
     const int kb = it.key_begin, ke = it.key_end;
 
-    const int wr0 = it.row_begin + wave * PS_PRE_ROWS_PER_WAVE;
+    const int wr0 = it.row_begin + wave * RPW;
     const bool active = wr0 < it.row_end;
-    const int wr_last = min(wr0 + PS_PRE_ROWS_PER_WAVE, it.row_end) - 1;
+    const int wr_last = min(wr0 + RPW, it.row_end) - 1;
     const int lim_lo = nc + wr0 / g;      // smallest visibility limit among the wave's rows
     const int lim_hi = nc + wr_last / g;  // largest
 
@@ -979,7 +979,7 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
     }
 
     // final output: normalise, round, transpose through LDS, write rows
-    T *so = reinterpret_cast<T *>(wave < 2 ? ring0 : ring1) + (wave & 1) * PS_PRE_ROWS_PER_WAVE * D;
+    T *so = reinterpret_cast<T *>(wave < 2 ? ring0 : ring1) + (wave & 1) * RPW * D;
     if (active) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -997,7 +997,7 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
     if (!active) return;
     constexpr int OCPR = D * ELT / 16;
     const uint8_t *sob = reinterpret_cast<const uint8_t *>(so);
-    for (int x = lane; x < PS_PRE_ROWS_PER_WAVE * OCPR; x += 64) {
+    for (int x = lane; x < RPW * OCPR; x += 64) {
         const int row = x / OCPR, ch = x - row * OCPR;
         const int r = wr0 + row;
         if (r >= it.row_end) continue;
@@ -1045,10 +1045,12 @@ __global__ __launch_bounds__(256) void ps_merge_kernel(const ps_attn_launch a) {
 // Launchers
 
 // Prefill kernel shape (tuning knob, PS_PREFILL_VARIANT): 0 = 64-key tiles
-// in a two-stage ring at two waves per SIMD (default for 16-bit data);
-// 1 = 32-key tiles in a three-stage ring; 2 = 32-key tiles in a two-stage
-// ring; 3 = 64-key tiles with a 512-register budget at one wave per SIMD.
-// fp32 rows always take 32-key tiles in two stages.
+// in a two-stage ring, 32 rows per wave at two waves per SIMD (default for
+// 16-bit data); 1 = 32-key tiles in a three-stage ring; 2 = 32-key tiles in
+// a two-stage ring; 3 = 64-key tiles, 32 rows per wave at one wave per SIMD
+// (512 registers). fp32 rows always take 32-key tiles in two stages. (64
+// rows per wave, RPW = 64, halves the LDS reads per MFMA but spills at
+// head_dim 128 and measured slower.)
 int prefill_variant() {
     static const int v = [] {
         const char *e = std::getenv("PS_PREFILL_VARIANT");
@@ -1056,6 +1058,17 @@ int prefill_variant() {
     }();
     return v;
 }
+
+}  // namespace psk
+
+// Packed rows per prefill work item for the kernel shape the launcher will
+// pick (the planner cuts items to match).
+int ps_prefill_rows(int dtype) {
+    (void)dtype;  // every shape launched today takes 32 rows per wave
+    return PS_PRE_WAVES * 32;
+}
+
+namespace psk {
 
 template <class DT, int D>
 hipError_t launch_attention_t(const ps_attn_launch &a, hipStream_t st) {
@@ -1074,20 +1087,20 @@ hipError_t launch_attention_t(const ps_attn_launch &a, hipStream_t st) {
     if (a.n_prefill > 0) {
         const dim3 grid(a.n_prefill), block(256);
         if constexpr (DT::ELT == 4) {
-            hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 2>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 2, 32>), grid, block, 0, st, a);
         } else {
             switch (prefill_variant()) {
                 case 1:
-                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 3>), grid, block, 0, st, a);
+                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 3, 32>), grid, block, 0, st, a);
                     break;
                 case 2:
-                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 2>), grid, block, 0, st, a);
+                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 2, 32>), grid, block, 0, st, a);
                     break;
                 case 3:
-                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE, 1, 2>), grid, block, 0, st, a);
+                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE, 1, 2, 32>), grid, block, 0, st, a);
                     break;
                 default:
-                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE, 2, 2>), grid, block, 0, st, a);
+                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE, 2, 2, 32>), grid, block, 0, st, a);
             }
         }
     }

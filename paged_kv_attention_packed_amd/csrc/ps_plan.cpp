@@ -175,10 +175,11 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         // Slices are long (>= 2048 keys): a split costs a merge launch and
         // partial traffic, which only pays off against long contexts; very
         // long steps are cut into about 512 items (two per CU).
+        const int64_t pre_rows = ps_prefill_rows(pool->dtype);
         int64_t dec_keys = 0, pre_keys = 0, pre_tiles = 0;
         for (int32_t s = 0; s < S; ++s) {
             const int64_t rows = (int64_t)g * q_lens[s], c = num_computed_tokens[s];
-            const int64_t rb = is_dec[s] ? PS_DEC_MAX_ROWS : PS_PRE_ROWS;
+            const int64_t rb = is_dec[s] ? PS_DEC_MAX_ROWS : pre_rows;
             for (int64_t r0 = 0; r0 < rows; r0 += rb) {
                 const int64_t r1 = std::min(rows, r0 + rb);
                 const int64_t kmax = c + (r1 - 1) / g + 1;
@@ -204,7 +205,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         for (int32_t s = 0; s < S; ++s) {
             const int64_t rows = (int64_t)g * q_lens[s], c = num_computed_tokens[s];
             const bool d = is_dec[s];
-            const int64_t rb = d ? PS_DEC_MAX_ROWS : PS_PRE_ROWS;
+            const int64_t rb = d ? PS_DEC_MAX_ROWS : pre_rows;
             for (int32_t j = 0; j < Hkv; ++j) {
                 for (int64_t r0 = 0; r0 < rows; r0 += rb) {
                     const int64_t r1 = std::min(rows, r0 + rb);
