@@ -176,7 +176,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         // partial traffic, which only pays off against long contexts; very
         // long steps are cut into about 512 items (two per CU).
         const int64_t pre_rows = ps_prefill_rows(pool->dtype);
-        int64_t dec_keys = 0, pre_keys = 0, pre_tiles = 0;
+        int64_t dec_keys = 0, pre_kmax = 0, pre_tiles = 0;
         for (int32_t s = 0; s < S; ++s) {
             const int64_t rows = (int64_t)g * q_lens[s], c = num_computed_tokens[s];
             const int64_t rb = is_dec[s] ? PS_DEC_MAX_ROWS : pre_rows;
@@ -184,7 +184,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                 const int64_t r1 = std::min(rows, r0 + rb);
                 const int64_t kmax = c + (r1 - 1) / g + 1;
                 if (is_dec[s]) dec_keys += kmax * Hkv;
-                else { pre_keys += kmax * Hkv; pre_tiles += Hkv; }
+                else { pre_kmax = std::max(pre_kmax, kmax); pre_tiles += Hkv; }
             }
         }
         const int64_t dec_split = std::min<int64_t>(
@@ -192,12 +192,17 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
             round_up(std::max<int64_t>(PS_BLOCK, env_int("PS_DECODE_SPLIT",
                                                          std::max<int64_t>(2048, round_up(ceil_div(dec_keys, 512), 128)))),
                      PS_BLOCK));
+        // Prefill: aim for three full rounds of resident workgroups (256 CUs
+        // x 2 = 512): each (row block, KV head) gets at most 1536 / blocks
+        // slices, sized from the longest key range so that no block gets
+        // more (a partly filled last round leaves CUs idle). A slice shorter
+        // than ~512 keys costs more in partials (a 128-row tile's partials
+        // weigh as much as ~500 keys of K/V) than it balances.
+        const int64_t pre_slices = std::max<int64_t>(1, 1536 / std::max<int64_t>(1, pre_tiles));
         const int64_t pre_split = env_int(
             "PS_PREFILL_SPLIT",
-            // only long key ranges are worth splitting: the partials of a
-            // 128-row tile cost as much traffic as ~500 keys of K/V
-            pre_tiles >= 256 ? INT32_MAX
-                             : std::max<int64_t>(4096, round_up(ceil_div(pre_keys, 512), PS_PRE_TILE)));
+            pre_tiles >= 512 ? INT32_MAX
+                             : std::max<int64_t>(512, round_up(ceil_div(pre_kmax, pre_slices), PS_PRE_TILE)));
 
         std::vector<int64_t> bounds;
         int64_t ws_rows = 0;
