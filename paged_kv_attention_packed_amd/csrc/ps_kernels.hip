@@ -382,8 +382,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
         for (int t = 0; t < NT; ++t) o[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // a second tile in flight does not fit the registers for fp32 rows of 128
-    constexpr bool DOUBLE_BUFFER = RT == 1 && !(ELT == 4 && D == 128);
+    // A second tile in flight fits the registers for one row tile (except
+    // fp32 rows of 128), and for two row tiles of 16-bit rows of 64.
+    constexpr bool DOUBLE_BUFFER = (RT == 1 && !(ELT == 4 && D == 128)) || (RT == 2 && ELT == 2 && D == 64);
     constexpr int NBUF = DOUBLE_BUFFER ? 2 : 1;
     u32x4 kf[NBUF][2][KU4];
     uint32_t vr[NBUF][8][VW];
