@@ -326,17 +326,22 @@ __global__ __launch_bounds__(256) void ps_copy_blocks_kernel(const u32x4 *__rest
 // trip (each wave takes every NW-th 32-key tile); the register budget
 // allows 2 waves per SIMD up to 8 waves and 4 per SIMD at 16.
 template <class DT, int D, int RT, int NW>
-__global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(const ps_attn_launch a) {
+struct DecodeLds {
+    float o[NW][RT * 16][D];   // per-wave partial outputs, merged at the end
+    float m[NW][RT * 16];
+    float l[NW][RT * 16];
+    int32_t bt[PS_DEC_MAX_SPLIT / PS_BLOCK];  // the item's block ids
+};
+
+template <class DT, int D, int RT, int NW>
+__device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, DecodeLds<DT, D, RT, NW> &sh) {
     using G = Geo<DT, D>;
     using T = typename DT::T;
     constexpr int ELT = G::ELT, KU4 = G::KU4, VW = G::VW, NT = G::NT, EPL = G::EPL;
     constexpr int ROWS = RT * 16;
 
-    __shared__ float sm_o[NW][ROWS][D];
-    __shared__ float sm_m[NW][ROWS];
-    __shared__ float sm_l[NW][ROWS];
 
-    const ps_item it = a.decode_items[blockIdx.x];
+    const ps_item it = a.decode_items[item];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps tile math scalar
     const int c = lane & 15, q4 = lane >> 4;
@@ -358,7 +363,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
     // reads its two ids there instead of waiting on a scalar load from the
     // table. The staging loads are issued before the first tile's, so
     // waiting for them does not wait for K/V.
-    __shared__ int32_t sbt[PS_DEC_MAX_SPLIT / PS_BLOCK];
+    int32_t *const sbt = sh.bt;
     constexpr int SPT = (PS_DEC_MAX_SPLIT / PS_BLOCK + 64 * NW - 1) / (64 * NW);
     const int nb = (ke - kb + PS_BLOCK - 1) / PS_BLOCK;
     const int32_t *btk = bt + (kb >> 4);
@@ -487,7 +492,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
     // Items start their walk over the key range at different tiles, so that
     // items sharing prefix blocks do not all ask for the same lines at once
     // (softmax order is free; the order is a fixed function of the item).
-    const int rot = ntiles > 1 ? (int)((blockIdx.x * 13u) % (unsigned)ntiles) : 0;
+    const int rot = ntiles > 1 ? (int)(((unsigned)item * 13u) % (unsigned)ntiles) : 0;
     auto key0 = [&](int t) {
         int u = t + rot;
         u -= u >= ntiles ? ntiles : 0;
@@ -553,10 +558,10 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sm_o[wave][rt * 16 + c][EPL * (4 * q4 + i) + t] = o[rt][t][i];
+            for (int i = 0; i < 4; ++i) sh.o[wave][rt * 16 + c][EPL * (4 * q4 + i) + t] = o[rt][t][i];
         if (q4 == 0) {
-            sm_m[wave][rt * 16 + c] = m[rt];
-            sm_l[wave][rt * 16 + c] = l[rt];
+            sh.m[wave][rt * 16 + c] = m[rt];
+            sh.l[wave][rt * 16 + c] = l[rt];
         }
     }
     __syncthreads();
@@ -570,7 +575,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
     float mw[NW], M = kNegInf;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        mw[w] = sm_m[w][row];
+        mw[w] = sh.m[w][row];
         M = fmaxf(M, mw[w]);
     }
     const float muse = M == kNegInf ? 0.f : M;
@@ -580,9 +585,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         const float f = fast_exp2(mw[w] - muse);
-        L += sm_l[w][row] * f;
+        L += sh.l[w][row] * f;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) acc[e] += sm_o[w][row][d0 + e] * f;
+        for (int e = 0; e < EPT; ++e) acc[e] += sh.o[w][row][d0 + e] * f;
     }
     if (it.partial_row < 0) {
         const int tok = r / g;
@@ -600,6 +605,12 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
             a.ws_l[pr] = L;
         }
     }
+}
+
+template <class DT, int D, int RT, int NW>
+__global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(const ps_attn_launch a) {
+    __shared__ DecodeLds<DT, D, RT, NW> L;
+    decode_item<DT, D, RT, NW>(a, blockIdx.x, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -687,8 +698,17 @@ __device__ inline void lds_row_words(const uint8_t *rowp, int row, int off, uint
 
 // TK: keys per tile; OCC: waves per SIMD the register budget is sized for
 // (1: 512 registers, accumulators may live in AGPRs; 2: 256 registers)
-template <class DT, int D, int TK, int OCC, int NST, int RPW>
-__global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_launch a) {
+template <class DT, int D, int TK, int NST>
+struct PrefillLds {
+    static constexpr int STAGEB = 2 * TK * D * DT::ELT;  // one ring stage: K tile, then V tile
+    __attribute__((aligned(1024))) uint8_t ring0[STAGEB];
+    __attribute__((aligned(1024))) uint8_t ring1[STAGEB];
+    __attribute__((aligned(1024))) uint8_t ring2[NST == 3 ? STAGEB : 1024];
+    int32_t bt[PS_PRE_MAX_KEYS / PS_BLOCK];  // the item's block ids
+};
+
+template <class DT, int D, int TK, int NST, int RPW>
+__device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, PrefillLds<DT, D, TK, NST> &sh) {
     using G = Geo<DT, D>;
     using T = typename DT::T;
     constexpr int ELT = G::ELT, KU4 = G::KU4, VW = G::VW, NT = G::NT, EPL = G::EPL;
@@ -702,19 +722,18 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
     static_assert(CPR >= 8 && TILEB % 4096 == 0, "tile geometry");
     static_assert(2 * RPW * D * ELT <= STAGEB, "output staging fits the ring");
 
-    // the ring stages are separate objects so the compiler can tell a read
-    // of one from the DMA still filling another
     static_assert(NST == 2 || NST == 3, "ring stages");
-    __shared__ __attribute__((aligned(1024))) uint8_t ring0[STAGEB];
-    __shared__ __attribute__((aligned(1024))) uint8_t ring1[STAGEB];
-    __shared__ __attribute__((aligned(1024))) uint8_t ring2[NST == 3 ? STAGEB : 1024];
+    static_assert(PrefillLds<DT, D, TK, NST>::STAGEB == STAGEB, "stage size");
+    uint8_t *const ring0 = sh.ring0;
+    uint8_t *const ring1 = sh.ring1;
+    uint8_t *const ring2 = sh.ring2;
     auto stage = [&](auto sc) -> uint8_t * {
         constexpr int st = decltype(sc)::value;
         return st == 0 ? ring0 : st == 1 ? ring1 : ring2;
     };
-    __shared__ int32_t sbt[PS_PRE_MAX_KEYS / PS_BLOCK];  // the item's block ids
+    int32_t *const sbt = sh.bt;
 
-    const ps_item it = a.prefill_items[blockIdx.x];
+    const ps_item it = a.prefill_items[item];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, q4 = lane >> 4;
@@ -1009,6 +1028,31 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
     }
 }
 
+template <class DT, int D, int TK, int OCC, int NST, int RPW>
+__global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_launch a) {
+    __shared__ PrefillLds<DT, D, TK, NST> L;
+    prefill_item<DT, D, TK, NST, RPW>(a, blockIdx.x, L);
+}
+
+// Decode and prefill items of one step in a single launch, so that the
+// memory-bound decode items and the MFMA-bound prefill items share the
+// CUs instead of running one kernel after the other. Block b < 2 min(nd,
+// np) alternates decode / prefill items (each CU starts with one of each),
+// the remaining blocks take what is left. Decode items run 4 waves.
+template <class DT, int D, int RT>
+__global__ __launch_bounds__(256, 2) void ps_mixed_kernel(const ps_attn_launch a) {
+    __shared__ union {
+        DecodeLds<DT, D, RT, 4> d;
+        PrefillLds<DT, D, PS_PRE_TILE, 2> p;
+    } L;
+    const int nd = a.n_decode, np = a.n_prefill, m = min(nd, np);
+    const int b = blockIdx.x;
+    const bool dec = b < 2 * m ? (b & 1) == 0 : nd > np;
+    const int idx = b < 2 * m ? b >> 1 : m + (b - 2 * m);
+    if (dec) decode_item<DT, D, RT, 4>(a, idx, L.d);
+    else prefill_item<DT, D, PS_PRE_TILE, 2, 32>(a, idx, L.p);
+}
+
 // ---------------------------------------------------------------------------
 // Split-K merge: out = sum_i acc_i 2^(m_i - M) / sum_i l_i 2^(m_i - M),
 // M = max_i m_i. One workgroup per chunk of rows of one split set; each
@@ -1071,8 +1115,30 @@ int ps_prefill_rows(int dtype) {
 
 namespace psk {
 
+// Decode and prefill items in one launch when a step has both (tuning knob,
+// PS_MIXED=0 launches them one after the other).
+bool mixed_launch() {
+    static const bool v = [] {
+        const char *e = std::getenv("PS_MIXED");
+        return !(e && std::atoi(e) == 0);
+    }();
+    return v;
+}
+
 template <class DT, int D>
 hipError_t launch_attention_t(const ps_attn_launch &a, hipStream_t st) {
+    if constexpr (DT::ELT == 2) {
+        if (a.n_decode > 0 && a.n_prefill > 0 && prefill_variant() == 0 && mixed_launch()) {
+            const dim3 grid(a.n_decode + a.n_prefill), block(256);
+            if (a.decode_row_tiles == 2)
+                hipLaunchKernelGGL((ps_mixed_kernel<DT, D, 2>), grid, block, 0, st, a);
+            else
+                hipLaunchKernelGGL((ps_mixed_kernel<DT, D, 1>), grid, block, 0, st, a);
+            if (a.n_merge > 0)
+                hipLaunchKernelGGL((ps_merge_kernel<DT, D>), dim3(a.n_merge), dim3(256), 0, st, a);
+            return hipGetLastError();
+        }
+    }
     if (a.n_decode > 0) {
         if (a.decode_row_tiles == 2) {
             hipLaunchKernelGGL((ps_decode_kernel<DT, D, 2, 4>), dim3(a.n_decode), dim3(256), 0, st, a);
