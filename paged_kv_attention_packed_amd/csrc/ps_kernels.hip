@@ -363,13 +363,21 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     // reads its two ids there instead of waiting on a scalar load from the
     // table. The staging loads are issued before the first tile's, so
     // waiting for them does not wait for K/V.
+    // A second tile in flight fits the registers for one row tile (except
+    // fp32 rows of 128), and for two row tiles of 16-bit rows of 64.
+    constexpr bool DOUBLE_BUFFER = (RT == 1 && !(ELT == 4 && D == 128)) || (RT == 2 && ELT == 2 && D == 64);
+    // Short items (no wave gets a tile past the ones it takes from the
+    // table) skip the staging and its barrier.
     int32_t *const sbt = sh.bt;
     constexpr int SPT = (PS_DEC_MAX_SPLIT / PS_BLOCK + 64 * NW - 1) / (64 * NW);
     const int nb = (ke - kb + PS_BLOCK - 1) / PS_BLOCK;
+    const bool staged = (ke - kb + PS_DEC_TILE - 1) / PS_DEC_TILE > (DOUBLE_BUFFER ? 2 : 1) * NW;
     const int32_t *btk = bt + (kb >> 4);
     int32_t stg[SPT];
+    if (staged) {
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) stg[i] = btk[min(tid + i * 64 * NW, nb - 1)];
+        for (int i = 0; i < SPT; ++i) stg[i] = btk[min(tid + i * 64 * NW, nb - 1)];
+    }
 
     u32x4 qf[RT][KU4];
     int lim[RT];
@@ -387,9 +395,6 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
         for (int t = 0; t < NT; ++t) o[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // A second tile in flight fits the registers for one row tile (except
-    // fp32 rows of 128), and for two row tiles of 16-bit rows of 64.
-    constexpr bool DOUBLE_BUFFER = (RT == 1 && !(ELT == 4 && D == 128)) || (RT == 2 && ELT == 2 && D == 64);
     constexpr int NBUF = DOUBLE_BUFFER ? 2 : 1;
     u32x4 kf[NBUF][2][KU4];
     uint32_t vr[NBUF][8][VW];
@@ -506,10 +511,12 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     if (ti < ntiles) load_tile(B0{}, key0(ti), FromTable{});
     if constexpr (DOUBLE_BUFFER)
         if (ti + NW < ntiles) load_tile(B1{}, key0(ti + NW), FromTable{});
+    if (staged) {
 #pragma unroll
-    for (int i = 0; i < SPT; ++i)
-        if (tid + i * 64 * NW < nb) sbt[tid + i * 64 * NW] = stg[i];
-    lds_barrier();
+        for (int i = 0; i < SPT; ++i)
+            if (tid + i * 64 * NW < nb) sbt[tid + i * 64 * NW] = stg[i];
+        lds_barrier();
+    }
     if constexpr (!DOUBLE_BUFFER) {
         // two row tiles leave no registers for a second tile in flight;
         // the other resident waves cover the load latency
