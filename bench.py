@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA, TFLOP/s
+FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 matrix, TFLOP/s
 LLC_BYTES = 256 << 20          # Infinity Cache
 ROTATE_TARGET = 1 << 30        # bytes touched between reuses of one pool copy
 
@@ -509,9 +510,37 @@ def main():
         except (OSError, ValueError, KeyError):
             traffic = None
     flops = info["flops_decode"] + info["flops_prefill"]
-    kernels = ([f"ps_decode_kernel x{info['decode_items']}"] if info["decode_items"] else []) + \
-              ([f"ps_prefill_kernel x{info['prefill_items']}"] if info["prefill_items"] else []) + \
-              ([f"ps_merge_kernel x{info['merge_items']}"] if info["merge_items"] else [])
+    nd, npf = info["decode_items"], info["prefill_items"]
+    # 16-bit steps with both kinds of item run them in one launch (the
+    # library's default kernel shape; PS_MIXED=0 or another prefill variant
+    # launches them one after the other)
+    mixed = (nd > 0 and npf > 0 and step.dtype_name != "f32"
+             and os.environ.get("PS_MIXED", "1") != "0"
+             and os.environ.get("PS_PREFILL_VARIANT", "0") == "0")
+    if mixed:
+        kernels = [f"ps_mixed_kernel x{nd + npf} ({nd} decode + {npf} prefill items)"]
+    else:
+        kernels = ([f"ps_decode_kernel x{nd}"] if nd else []) + \
+                  ([f"ps_prefill_kernel x{npf}"] if npf else [])
+    if info["merge_items"]:
+        kernels.append(f"ps_merge_kernel x{info['merge_items']}")
+    # the launch's bound is the larger of its two ideal times: algorithmic
+    # bytes at HBM peak, or its QK^T and PV flops at dense 16-bit MFMA peak
+    # (fp32 rows run v_mfma_f32_16x16x4f32, priced at the fp32 matrix peak)
+    mfma_peak = MFMA_PEAK_TFLOPS if step.dtype_name != "f32" else FP32_PEAK_TFLOPS
+    t_hbm = dom_bytes / (HBM_PEAK_GBS * 1e9)
+    dom_flops = flops if not fused else info["flops_decode"]
+    t_mfma = dom_flops / (mfma_peak * 1e12)
+    hbm_line = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    tflops_dom = dom_flops / (ms_dom * 1e-3) / 1e12
+    mfma_line = {"bound": "mfma", "achieved": round(tflops_dom, 1), "peak": mfma_peak,
+                 "unit": "TFLOP/s", "frac": round(tflops_dom / mfma_peak, 4)}
+    if t_mfma > t_hbm:
+        roofline, other = dict(mfma_line), hbm_line
+    else:
+        roofline, other = dict(hbm_line), mfma_line
+    roofline["traffic"] = traffic
 
     result = {
         "metric": "packed paged-attn query tok/s + KV-read HBM GB/s (% peak), 1 MI355X",
@@ -530,9 +559,8 @@ def main():
                    "num_q_heads": step.num_q_heads, "num_kv_heads": step.num_kv_heads,
                    "head_dim": step.head_dim, "block_size": 16, "num_blocks": step.num_blocks,
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+        "roofline": roofline,
+        "roofline_other_bound": other,
         "dominant": {"call": dom_call, "kernels": kernels,
                      "algorithmic_bytes_per_launch": dom_bytes,
                      "us_per_launch": round(ms_dom * 1e3, 3)},
