@@ -19,8 +19,17 @@ struct ps_item {
     int32_t key_end;     // one past the last key position (<= context length)
     int32_t partial_row; // -1: write the output; else first workspace row of this item's partials
     int32_t flags;       // PS_ITEM_* bits
+    // Copies of the sequence's offsets, so that a workgroup's first
+    // dependent loads need only the item.
+    int32_t q_start;      // query_start_loc[seq]
+    int32_t num_computed; // num_computed_tokens[seq]
+    // Decode items walk their 32-key tiles starting at tile `rot` (mod the
+    // tile count): items that share prefix blocks then do not request the
+    // same lines at the same time (softmax order is free). Prefill: 0.
+    int32_t rot;
+    int32_t pad;
 };
-static_assert(sizeof(ps_item) == 32, "ps_item layout");
+static_assert(sizeof(ps_item) == 48, "ps_item layout");
 // The one item per (sequence, KV head) that holds the sequence's last keys
 // (last row range, last key slice): with the scatter fused into the
 // decode launch it writes the step's new K/V rows of its KV head.
@@ -36,7 +45,7 @@ struct ps_merge {
     int32_t partial_row; // split i's row r is partial_row + i * split_stride + (r - row_begin)
     int32_t num_splits;
     int32_t split_stride; // rows of each split's partial block
-    int32_t pad;
+    int32_t q_start;      // query_start_loc[seq]
 };
 // rows one merge workgroup covers: 256 threads, each 4 elements of a row
 inline int ps_merge_rows(int head_dim) { return 1024 / head_dim; }
@@ -47,6 +56,10 @@ constexpr int PS_BLOCK = 16;            // tokens per pool block
 constexpr int PS_DEC_TILE = 32;         // keys per decode-kernel wave iteration
 constexpr int PS_DEC_MAX_ROWS = 32;     // packed rows per decode work item (two 16-row MFMA tiles)
 constexpr int PS_DEC_MAX_SPLIT = 16384; // keys per decode work item at most
+// Block ids of a decode item's first tiles in walk order (two per 32-key
+// tile), laid out per item in the metadata: a wave's first tiles read
+// their ids there, with no wait on the block table's row.
+constexpr int PS_DEC_HEAD_TILES = 16;
 constexpr int PS_PRE_TILE = 64;         // keys per prefill LDS tile
 constexpr int PS_PRE_WAVES = 4;         // waves per prefill work item
 constexpr int PS_PRE_ROWS_PER_WAVE = 32;
@@ -84,6 +97,7 @@ struct ps_attn_launch {
     const ps_item *decode_items;
     const ps_item *prefill_items;
     const ps_merge *merges;
+    const int32_t *decode_head;   // [n_decode][2 * PS_DEC_HEAD_TILES] block ids
     float *ws_m;
     float *ws_l;
     float *ws_acc;

@@ -347,7 +347,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     const int c = lane & 15, q4 = lane >> 4;
     const int s = it.seq, j = it.kv_head;
     const int g = a.num_q_heads / a.num_kv_heads;
-    const int qs0 = a.query_start_loc[s], nc = a.num_computed[s];
+    const int qs0 = it.q_start, nc = it.num_computed;
     const int32_t *bt = a.block_tables + (int64_t)s * a.bt_stride;
     const int64_t rs = (int64_t)a.num_kv_heads * D;  // elements from one slot to the next
     const T *kp = static_cast<const T *>(a.pool_k) + a.layer_offset + (int64_t)j * D;
@@ -399,11 +399,14 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     u32x4 kf[NBUF][2][KU4];
     uint32_t vr[NBUF][8][VW];
 
-    // K/V of keys [k0, k0 + 32): two pool blocks. Block ids are read with
-    // scalar loads (k0 is wave-uniform), so the vector loads never wait on
-    // each other. Rows of an existing block past key_end are loaded (they
-    // are in bounds) and zeroed or masked at use.
-    auto load_tile = [&](auto bufc, int k0, auto from_lds) {
+    // K/V of walk-order tile t, keys [k0, k0 + 32): two pool blocks. Block
+    // ids are read with scalar loads (t is wave-uniform), so the vector
+    // loads never wait on each other: a wave's first tiles from the item's
+    // head ids (they need nothing but the item's index), later ones from
+    // LDS. Rows of an existing block past key_end are loaded (they are in
+    // bounds) and zeroed or masked at use.
+    const int2 *head = reinterpret_cast<const int2 *>(a.decode_head) + (int64_t)item * PS_DEC_HEAD_TILES;
+    auto load_tile = [&](auto bufc, int t, int k0, auto from_lds) {
         constexpr int buf = decltype(bufc)::value;
         const bool has1 = k0 + 16 < ke;
         int64_t blk0, blk1;
@@ -411,6 +414,10 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
             const int li = (k0 - kb) >> 4;
             blk0 = __builtin_amdgcn_readfirstlane(sbt[li]);
             blk1 = has1 ? __builtin_amdgcn_readfirstlane(sbt[li + 1]) : blk0;
+        } else if (t < PS_DEC_HEAD_TILES) {
+            const int2 ids = head[t];
+            blk0 = ids.x;
+            blk1 = ids.y;
         } else {
             blk0 = bt[k0 >> 4];
             blk1 = has1 ? (int64_t)bt[(k0 >> 4) + 1] : blk0;
@@ -497,7 +504,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     // Items start their walk over the key range at different tiles, so that
     // items sharing prefix blocks do not all ask for the same lines at once
     // (softmax order is free; the order is a fixed function of the item).
-    const int rot = ntiles > 1 ? (int)(((unsigned)item * 13u) % (unsigned)ntiles) : 0;
+    const int rot = it.rot;
     auto key0 = [&](int t) {
         int u = t + rot;
         u -= u >= ntiles ? ntiles : 0;
@@ -508,9 +515,9 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     // ids from the table; they are in flight while the staged ids are
     // written. Waiting for the staging loads there waits for those tiles
     // too, which costs little: they were issued together.
-    if (ti < ntiles) load_tile(B0{}, key0(ti), FromTable{});
+    if (ti < ntiles) load_tile(B0{}, ti, key0(ti), FromTable{});
     if constexpr (DOUBLE_BUFFER)
-        if (ti + NW < ntiles) load_tile(B1{}, key0(ti + NW), FromTable{});
+        if (ti + NW < ntiles) load_tile(B1{}, ti + NW, key0(ti + NW), FromTable{});
     if (staged) {
 #pragma unroll
         for (int i = 0; i < SPT; ++i)
@@ -521,7 +528,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
         // two row tiles leave no registers for a second tile in flight;
         // the other resident waves cover the load latency
         for (; ti < ntiles; ti += NW) {
-            if (ti != wave) load_tile(B0{}, key0(ti), FromLds{});
+            if (ti != wave) load_tile(B0{}, ti, key0(ti), FromLds{});
             compute_tile(B0{}, key0(ti));
         }
     }
@@ -529,11 +536,11 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
         // tile ti + 2 NW streams into the buffer tile ti has just released
         while (ti < ntiles) {
             compute_tile(B0{}, key0(ti));
-            if (ti + 2 * NW < ntiles) load_tile(B0{}, key0(ti + 2 * NW), FromLds{});
+            if (ti + 2 * NW < ntiles) load_tile(B0{}, ti + 2 * NW, key0(ti + 2 * NW), FromLds{});
             ti += NW;
             if (ti >= ntiles) break;
             compute_tile(B1{}, key0(ti));
-            if (ti + 2 * NW < ntiles) load_tile(B1{}, key0(ti + 2 * NW), FromLds{});
+            if (ti + 2 * NW < ntiles) load_tile(B1{}, ti + 2 * NW, key0(ti + 2 * NW), FromLds{});
             ti += NW;
         }
     }
@@ -746,7 +753,7 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
     const int c = lane & 15, q4 = lane >> 4;
     const int s = it.seq, j = it.kv_head;
     const int g = a.num_q_heads / a.num_kv_heads;
-    const int qs0 = a.query_start_loc[s], nc = a.num_computed[s];
+    const int qs0 = it.q_start, nc = it.num_computed;
     const int32_t *bt = a.block_tables + (int64_t)s * a.bt_stride;
     const int64_t rs = (int64_t)a.num_kv_heads * D;
     const T *kp = static_cast<const T *>(a.pool_k) + a.layer_offset + (int64_t)j * D;
@@ -1087,7 +1094,7 @@ __global__ __launch_bounds__(256) void ps_merge_kernel(const ps_attn_launch a) {
     }
     const int tok = r / g;
     const int h = mg.kv_head * g + (r - tok * g);
-    T *op = static_cast<T *>(a.out) + ((int64_t)(a.query_start_loc[mg.seq] + tok) * a.num_q_heads + h) * D + d0;
+    T *op = static_cast<T *>(a.out) + ((int64_t)(mg.q_start + tok) * a.num_q_heads + h) * D + d0;
     const float inv = 1.f / L;
 #pragma unroll
     for (int e = 0; e < 4; ++e) op[e] = cvt_out(acc[e] * inv, DT{});

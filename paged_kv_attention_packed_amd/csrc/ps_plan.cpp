@@ -27,6 +27,7 @@ struct ps_plan {
     // the metadata blob, laid out exactly as it is copied to the device
     std::vector<uint8_t> blob;
     size_t off_qsl = 0, off_nc = 0, off_ctx = 0, off_slot = 0, off_pos = 0, off_bt = 0;
+    size_t off_dhead = 0;
     size_t off_dec = 0, off_pre = 0, off_mrg = 0;
     void *dev = nullptr;
     ps_plan_info info{};
@@ -207,7 +208,8 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         std::vector<int64_t> bounds;
         int64_t ws_rows = 0;
         int32_t dec_rt = 1;
-        for (int32_t s = 0; s < S; ++s) {
+        int32_t qs_run = 0;   // query_start_loc[s]
+        for (int32_t s = 0; s < S; qs_run += q_lens[s], ++s) {
             const int64_t rows = (int64_t)g * q_lens[s], c = num_computed_tokens[s];
             const bool d = is_dec[s];
             const int64_t rb = d ? PS_DEC_MAX_ROWS : pre_rows;
@@ -230,6 +232,12 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                         it.key_end = (int32_t)bounds[i + 1];
                         it.partial_row = ns > 1 ? (int32_t)(base + i * (r1 - r0)) : -1;
                         it.flags = r1 == rows && i == ns - 1 ? PS_ITEM_WRITES_NEW : 0;
+                        it.q_start = qs_run;
+                        it.num_computed = (int32_t)c;
+                        if (d) {
+                            const int64_t ntiles = ceil_div(it.key_end - it.key_begin, PS_DEC_TILE);
+                            it.rot = ntiles > 1 ? (int32_t)((dec.size() * 13) % (size_t)ntiles) : 0;
+                        }
                         (d ? dec : pre).push_back(it);
                     }
                     if (ns > 1) {
@@ -243,6 +251,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                             m.partial_row = (int32_t)(base + (q0 - r0));
                             m.num_splits = (int32_t)ns;
                             m.split_stride = (int32_t)(r1 - r0);
+                            m.q_start = qs_run;
                             mrg.push_back(m);
                         }
                         ws_rows += ns * (r1 - r0);
@@ -276,6 +285,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         p->off_dec = take(sizeof(ps_item) * dec.size());
         p->off_pre = take(sizeof(ps_item) * pre.size());
         p->off_mrg = take(sizeof(ps_merge) * mrg.size());
+        p->off_dhead = take(sizeof(int32_t) * 2 * PS_DEC_HEAD_TILES * dec.size());
         p->blob.assign(off, 0);
 
         int32_t *qsl = p->host<int32_t>(p->off_qsl);
@@ -300,6 +310,21 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         if (!dec.empty()) std::memcpy(p->host<ps_item>(p->off_dec), dec.data(), sizeof(ps_item) * dec.size());
         if (!pre.empty()) std::memcpy(p->host<ps_item>(p->off_pre), pre.data(), sizeof(ps_item) * pre.size());
         if (!mrg.empty()) std::memcpy(p->host<ps_merge>(p->off_mrg), mrg.data(), sizeof(ps_merge) * mrg.size());
+        // decode items' first tiles in walk order: tile t covers keys
+        // key_begin + 32 u .. +32, u = (t + rot) mod ntiles; a tile's second
+        // block past key_end repeats the first (never read)
+        int32_t *dh = p->host<int32_t>(p->off_dhead);
+        for (size_t i = 0; i < dec.size(); ++i) {
+            const ps_item &it = dec[i];
+            const int32_t *row = block_tables + (int64_t)it.seq * block_table_stride;
+            const int64_t ntiles = ceil_div(it.key_end - it.key_begin, PS_DEC_TILE);
+            for (int64_t t = 0; t < std::min<int64_t>(ntiles, PS_DEC_HEAD_TILES); ++t) {
+                const int64_t u = (t + it.rot) % ntiles, k0 = it.key_begin + u * PS_DEC_TILE;
+                const int32_t b0 = row[k0 / PS_BLOCK];
+                dh[i * 2 * PS_DEC_HEAD_TILES + 2 * t] = b0;
+                dh[i * 2 * PS_DEC_HEAD_TILES + 2 * t + 1] = k0 + PS_BLOCK < it.key_end ? row[k0 / PS_BLOCK + 1] : b0;
+            }
+        }
 
         // ---- algorithmic accounting
         ps_plan_info &I = p->info;
@@ -453,6 +478,7 @@ static ps_status prepare_attention(const void *q, const ps_pool *pool, const int
     a.decode_items = reinterpret_cast<const ps_item *>(dev + plan->off_dec);
     a.prefill_items = reinterpret_cast<const ps_item *>(dev + plan->off_pre);
     a.merges = reinterpret_cast<const ps_merge *>(dev + plan->off_mrg);
+    a.decode_head = reinterpret_cast<const int32_t *>(dev + plan->off_dhead);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     a.ws_m = wl.bytes ? reinterpret_cast<float *>(ws + wl.off_m) : nullptr;
     a.ws_l = wl.bytes ? reinterpret_cast<float *>(ws + wl.off_l) : nullptr;
