@@ -403,9 +403,18 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     // ids are read with scalar loads (t is wave-uniform), so the vector
     // loads never wait on each other: a wave's first tiles from the item's
     // head ids (they need nothing but the item's index), later ones from
-    // LDS. Rows of an existing block past key_end are loaded (they are in
-    // bounds) and zeroed or masked at use.
+    // LDS. A block's address is a scalar base plus a lane offset fixed for
+    // the whole item, so the loads take no vector address arithmetic. Rows
+    // of an existing block past key_end are loaded (they are in bounds) and
+    // zeroed or masked at use.
     const int2 *head = reinterpret_cast<const int2 *>(a.decode_head) + (int64_t)item * PS_DEC_HEAD_TILES;
+    const int64_t rsb = rs * ELT;                     // bytes from one slot (or token) to the next
+    const uint32_t koff = (uint32_t)(c * rsb + 16 * q4);   // + 64 u: the lane's K words
+    uint32_t voff[4];                                  // V row 4 q4 + i of a block, the lane's words
+#pragma unroll
+    for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((4 * q4 + i) * rsb + EPL * c * ELT);
+    const char *kpool = reinterpret_cast<const char *>(kp), *vpool = reinterpret_cast<const char *>(vp);
+    const char *knew = reinterpret_cast<const char *>(kn), *vnew = reinterpret_cast<const char *>(vn);
     auto load_tile = [&](auto bufc, int t, int k0, auto from_lds) {
         constexpr int buf = decltype(bufc)::value;
         const bool has1 = k0 + 16 < ke;
@@ -424,28 +433,49 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
         }
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
+            const int kbk = k0 + sb * 16;                // the block's first key
             const int64_t blk = sb ? blk1 : blk0;
-            if (sb == 0 || has1) {
-                const int pos = k0 + sb * 16 + c;
-                const T *p = pos >= new_lo && pos < ke ? kn + (int64_t)pos * rs : kp + (blk * 16 + c) * rs;
+            const char *kb_pool = kpool + blk * 16 * rsb, *vb_pool = vpool + blk * 16 * rsb;
+            if (kbk + 16 <= new_lo) {
+                // every row from the pool: scalar base + fixed lane offset
+                if (sb == 0 || has1) {
 #pragma unroll
-                for (int u = 0; u < KU4; ++u)
-                    kf[buf][sb][u] = *reinterpret_cast<const u32x4 *>(p + (u * 4 + q4) * (16 / ELT));
+                    for (int u = 0; u < KU4; ++u)
+                        kf[buf][sb][u] = *reinterpret_cast<const u32x4 *>(kb_pool + koff + 64 * u);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < KU4; ++u) kf[buf][sb][u] = u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) load_words<VW>(vb_pool + voff[i], vr[buf][sb * 4 + i]);
             } else {
+                // the block holds keys of this step: rows in [new_lo, ke)
+                // come from k_new / v_new, whose token rows have the same
+                // stride as pool slots
+                const char *kb_new = knew + (int64_t)kbk * rsb, *vb_new = vnew + (int64_t)kbk * rsb;
+                if (sb == 0 || has1) {
+                    const int pos = kbk + c;
+                    const char *base = pos >= new_lo && pos < ke ? kb_new : kb_pool;
 #pragma unroll
-                for (int u = 0; u < KU4; ++u) kf[buf][sb][u] = u32x4{0u, 0u, 0u, 0u};
+                    for (int u = 0; u < KU4; ++u)
+                        kf[buf][sb][u] = *reinterpret_cast<const u32x4 *>(base + koff + 64 * u);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < KU4; ++u) kf[buf][sb][u] = u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int pos = kbk + 4 * q4 + i;
+                    const char *base = pos >= new_lo && pos < ke ? vb_new : vb_pool;
+                    load_words<VW>(base + voff[i], vr[buf][sb * 4 + i]);
+                }
             }
-        }
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int64_t blk = (jj >> 2) ? blk1 : blk0;
-            const int rw = 4 * q4 + (jj & 3);
-            const int pos = k0 + (jj >> 2) * 16 + rw;
-            const T *p = pos >= new_lo && pos < ke ? vn + (int64_t)pos * rs : vp + (blk * 16 + rw) * rs;
-            load_words<VW>(p + EPL * c, vr[buf][jj]);
         }
     };
 
+    // keys below vis_all are visible to every row of the item (the first
+    // row's query sits at position nc + row_begin / g)
+    const int vis_all = min(ke, nc + it.row_begin / g + 1);
     auto compute_tile = [&](auto bufc, int k0) {
         constexpr int buf = decltype(bufc)::value;
         float pv[RT][8];
@@ -454,11 +484,21 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
             f32x4 sacc[2];
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) sacc[sb] = qk_tile<DT, D>(kf[buf][sb], qf[rt]);
-            const int vis = min(ke - 1, lim[rt]) - k0 - 4 * q4;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pv[rt][sb * 4 + i] = sb * 16 + i <= vis ? sacc[sb][i] : kNegInf;
+                for (int i = 0; i < 4; ++i) pv[rt][sb * 4 + i] = sacc[sb][i];
+        }
+        if (k0 + PS_DEC_TILE > vis_all) {
+            // a tile on the causal diagonal or at the slice's end
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int vis = min(ke - 1, lim[rt]) - k0 - 4 * q4;
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pv[rt][sb * 4 + i] = sb * 16 + i <= vis ? pv[rt][sb * 4 + i] : kNegInf;
+            }
         }
         softmax_update(pv, a.scale_log2, m, l, o);
         if (k0 + PS_DEC_TILE > ke) {
