@@ -112,6 +112,11 @@ struct ps_attn_launch {
     int32_t decode_row_tiles;
     int32_t decode_waves;   // waves per decode workgroup (4, 8 or 16)
     float scale_log2;       // softmax scale * log2(e)
+    // g = num_q_heads / num_kv_heads, and r / g for 0 <= r < 2^31 as
+    // (r * g_magic) >> g_shift (see ps_group_divisor)
+    int32_t g;
+    uint32_t g_magic;
+    int32_t g_shift;
     // Scatter fused into the decode kernel (steps without prefill items):
     // keys at positions >= num_computed are read from k_new / v_new
     // ([T, Hkv, D]) and the item holding a sequence's last keys writes
@@ -122,6 +127,19 @@ struct ps_attn_launch {
     const void *v_new;
     const int32_t *slot_mapping;
 };
+
+// Division by the group size g with a multiply and a shift (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994):
+// with l = ceil(log2 g), s = 31 + l and m = floor(2^s / g) + 1, the error
+// e = m g - 2^s lies in (0, 2^l], so for 0 <= r < 2^31
+// r m / 2^s = r / g + r e / (g 2^s) with the last term below 1 / g, and
+// floor(r m / 2^s) = floor(r / g). m < 2^32.
+inline void ps_group_divisor(int32_t g, uint32_t *magic, int32_t *shift) {
+    int32_t l = 0;
+    while ((int64_t(1) << l) < g) ++l;
+    *shift = 31 + l;
+    *magic = (uint32_t)(((uint64_t)1 << (31 + l)) / (uint64_t)g + 1);
+}
 
 // Rotary embedding + KV scatter launch (ps_rope.hip). The pair frequencies
 // travel by value in the kernel arguments, so the call needs no device

@@ -232,13 +232,19 @@ __device__ inline void softmax_update(float (&sv)[RT][NS], float c, float (&m)[R
     }
 }
 
+// r / g for 0 <= r < 2^31 (g = num_q_heads / num_kv_heads): a multiply
+// and a shift with constants the host derived.
+__device__ inline int div_g(const ps_attn_launch &a, int r) {
+    return (int)(((uint64_t)(uint32_t)r * a.g_magic) >> a.g_shift);
+}
+
 // Which query row a lane's packed row stands for, its visibility limit and
 // its Q fragment.
 template <class DT, int D>
 __device__ inline void load_q_row(const ps_attn_launch &a, int r, int row_end, int g, int kv_head,
                                   int qs0, int nc, int q4, u32x4 (&qf)[Geo<DT, D>::KU4], int &lim) {
     if (r < row_end) {
-        const int tok = r / g;
+        const int tok = div_g(a, r);
         const int h = kv_head * g + (r - tok * g);
         lim = nc + tok;
         const typename DT::T *qp =
@@ -340,13 +346,27 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     constexpr int ELT = G::ELT, KU4 = G::KU4, VW = G::VW, NT = G::NT, EPL = G::EPL;
     constexpr int ROWS = RT * 16;
 
-
-    const ps_item it = a.decode_items[item];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps tile math scalar
+    // The item, the block ids of the wave's first tiles and the launch's
+    // arguments, all needed before the first K/V load: the empty asm takes
+    // them as operands, so their scalar loads are issued together and
+    // waited for once instead of at first uses scattered over the prologue
+    // (scalar loads return out of order: every wait is a wait for all).
+    // It comes after the loads: a volatile asm counts as a possible memory
+    // write, and loads after it would not be scalar loads.
+    const ps_item it = a.decode_items[item];
+    const int2 *head = reinterpret_cast<const int2 *>(a.decode_head) + (int64_t)item * PS_DEC_HEAD_TILES;
+    const int2 hid0 = head[wave];
+    const int2 hid1 = head[min(wave + NW, PS_DEC_HEAD_TILES - 1)];
+    asm volatile("" ::"s"(it.seq), "s"(it.kv_head), "s"(it.row_begin), "s"(it.row_end), "s"(it.key_begin),
+                 "s"(it.key_end), "s"(it.partial_row), "s"(it.flags), "s"(it.q_start), "s"(it.num_computed),
+                 "s"(it.rot), "s"(hid0.x), "s"(hid0.y), "s"(hid1.x), "s"(hid1.y), "s"(a.pool_k), "s"(a.pool_v),
+                 "s"(a.layer_offset), "s"(a.block_tables), "s"(a.bt_stride), "s"(a.q), "s"(a.k_new),
+                 "s"(a.v_new), "s"(a.num_kv_heads), "s"(a.g), "s"(a.g_magic));
     const int c = lane & 15, q4 = lane >> 4;
     const int s = it.seq, j = it.kv_head;
-    const int g = a.num_q_heads / a.num_kv_heads;
+    const int g = a.g;
     const int qs0 = it.q_start, nc = it.num_computed;
     const int32_t *bt = a.block_tables + (int64_t)s * a.bt_stride;
     const int64_t rs = (int64_t)a.num_kv_heads * D;  // elements from one slot to the next
@@ -373,7 +393,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     const int nb = (ke - kb + PS_BLOCK - 1) / PS_BLOCK;
     const bool staged = (ke - kb + PS_DEC_TILE - 1) / PS_DEC_TILE > (DOUBLE_BUFFER ? 2 : 1) * NW;
     const int32_t *btk = bt + (kb >> 4);
-    int32_t stg[SPT];
+    int32_t stg[SPT] = {};
     if (staged) {
 #pragma unroll
         for (int i = 0; i < SPT; ++i) stg[i] = btk[min(tid + i * 64 * NW, nb - 1)];
@@ -407,7 +427,6 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     // the whole item, so the loads take no vector address arithmetic. Rows
     // of an existing block past key_end are loaded (they are in bounds) and
     // zeroed or masked at use.
-    const int2 *head = reinterpret_cast<const int2 *>(a.decode_head) + (int64_t)item * PS_DEC_HEAD_TILES;
     const int64_t rsb = rs * ELT;                     // bytes from one slot (or token) to the next
     const uint32_t koff = (uint32_t)(c * rsb + 16 * q4);   // + 64 u: the lane's K words
     uint32_t voff[4];                                  // V row 4 q4 + i of a block, the lane's words
@@ -423,8 +442,8 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
             const int li = (k0 - kb) >> 4;
             blk0 = __builtin_amdgcn_readfirstlane(sbt[li]);
             blk1 = has1 ? __builtin_amdgcn_readfirstlane(sbt[li + 1]) : blk0;
-        } else if (t < PS_DEC_HEAD_TILES) {
-            const int2 ids = head[t];
+        } else if (t < PS_DEC_HEAD_TILES) {   // t is wave or wave + NW
+            const int2 ids = t == wave ? hid0 : hid1;
             blk0 = ids.x;
             blk1 = ids.y;
         } else {
@@ -475,7 +494,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
 
     // keys below vis_all are visible to every row of the item (the first
     // row's query sits at position nc + row_begin / g)
-    const int vis_all = min(ke, nc + it.row_begin / g + 1);
+    const int vis_all = min(ke, nc + div_g(a, it.row_begin) + 1);
     auto compute_tile = [&](auto bufc, int k0) {
         constexpr int buf = decltype(bufc)::value;
         float pv[RT][8];
@@ -605,6 +624,12 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
         }
     }
 
+    // The staging registers stay allocated up to here: reused earlier,
+    // they would make the first tile's compute wait (at the join of the
+    // staged and unstaged paths) for every load in flight.
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) asm volatile("" ::"v"(stg[i]));
+
     // ---- merge the waves' states
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -644,7 +669,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
         for (int e = 0; e < EPT; ++e) acc[e] += sh.o[w][row][d0 + e] * f;
     }
     if (it.partial_row < 0) {
-        const int tok = r / g;
+        const int tok = div_g(a, r);
         const int h = j * g + (r - tok * g);
         T *op = static_cast<T *>(a.out) + ((int64_t)(qs0 + tok) * a.num_q_heads + h) * D + d0;
         const float inv = 1.f / L;
@@ -792,7 +817,7 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, q4 = lane >> 4;
     const int s = it.seq, j = it.kv_head;
-    const int g = a.num_q_heads / a.num_kv_heads;
+    const int g = a.g;
     const int qs0 = it.q_start, nc = it.num_computed;
     const int32_t *bt = a.block_tables + (int64_t)s * a.bt_stride;
     const int64_t rs = (int64_t)a.num_kv_heads * D;
@@ -803,8 +828,8 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
     const int wr0 = it.row_begin + wave * RPW;
     const bool active = wr0 < it.row_end;
     const int wr_last = min(wr0 + RPW, it.row_end) - 1;
-    const int lim_lo = nc + wr0 / g;      // smallest visibility limit among the wave's rows
-    const int lim_hi = nc + wr_last / g;  // largest
+    const int lim_lo = nc + div_g(a, wr0);      // smallest visibility limit among the wave's rows
+    const int lim_hi = nc + div_g(a, wr_last);  // largest
 
     u32x4 qf[RT][KU4];
     int lim[RT];
@@ -1075,7 +1100,7 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
         const int row = x / OCPR, ch = x - row * OCPR;
         const int r = wr0 + row;
         if (r >= it.row_end) continue;
-        const int tok = r / g;
+        const int tok = div_g(a, r);
         const int h = j * g + (r - tok * g);
         uint8_t *dst = static_cast<uint8_t *>(a.out) + (((int64_t)(qs0 + tok) * a.num_q_heads + h) * D) * ELT;
         reinterpret_cast<u32x4 *>(dst)[ch] = *reinterpret_cast<const u32x4 *>(sob + row * D * ELT + ch * 16);
@@ -1119,7 +1144,7 @@ __global__ __launch_bounds__(256) void ps_merge_kernel(const ps_attn_launch a) {
     const int row = threadIdx.x / (D / 4), d0 = (threadIdx.x % (D / 4)) * 4;
     const int r = mg.row_begin + row;
     if (r >= mg.row_end) return;
-    const int g = a.num_q_heads / a.num_kv_heads;
+    const int g = a.g;
     const int64_t p0 = (int64_t)mg.partial_row + row;
     float M = kNegInf;
     for (int sp = 0; sp < mg.num_splits; ++sp) M = fmaxf(M, a.ws_m[p0 + (int64_t)sp * mg.split_stride]);
@@ -1132,7 +1157,7 @@ __global__ __launch_bounds__(256) void ps_merge_kernel(const ps_attn_launch a) {
         L += a.ws_l[pr] * f;
         acc += *reinterpret_cast<const f32x4 *>(a.ws_acc + pr * D + d0) * f;
     }
-    const int tok = r / g;
+    const int tok = div_g(a, r);
     const int h = mg.kv_head * g + (r - tok * g);
     T *op = static_cast<T *>(a.out) + ((int64_t)(mg.q_start + tok) * a.num_q_heads + h) * D + d0;
     const float inv = 1.f / L;

@@ -498,6 +498,8 @@ static ps_status prepare_attention(const void *q, const ps_pool *pool, const int
     // one round trip; many items: 4 waves each fill the chip
     a.decode_waves = (int32_t)env_int("PS_DECODE_WAVES", plan->n_dec < 512 ? 8 : 4);
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.g = plan->Hq / plan->Hkv;
+    ps_group_divisor(a.g, &a.g_magic, &a.g_shift);
     a.num_slots = plan->num_blocks * PS_BLOCK;
     return PS_OK;
 }
