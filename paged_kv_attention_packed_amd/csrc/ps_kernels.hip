@@ -399,6 +399,34 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
         for (int i = 0; i < SPT; ++i) stg[i] = btk[min(tid + i * 64 * NW, nb - 1)];
     }
 
+    // Fused scatter: the item holding the sequence's last keys (last row
+    // range, last key slice) copies this step's K/V rows of its KV head
+    // into their slots; no item of this launch reads those slots from the
+    // pool. A thread's first 16-byte word and its slot are loaded here,
+    // ahead of the K/V tiles, and stored after the tiles: the copy then
+    // adds no load latency to the item's end.
+    constexpr int WPR = D * ELT / 16;   // 16-byte words per head row
+    const bool writer = fused && (it.flags & PS_ITEM_WRITES_NEW);
+    const int sc_units = writer ? 2 * (ke - nc) * WPR : 0;
+    const int64_t rw16 = rs * ELT / 16;   // 16-byte words from one slot (or token) to the next
+    auto sc_word = [&](int w, const u32x4 *&src, int &i, int &cw, int &which) {
+        which = w >= (ke - nc) * WPR;   // K words first, then V (w < sc_units)
+        const int r2 = w - which * (ke - nc) * WPR;
+        i = r2 / WPR;
+        cw = r2 - i * WPR;
+        src = reinterpret_cast<const u32x4 *>(which ? vn : kn) + (int64_t)(nc + i) * rw16 + cw;
+    };
+    u32x4 sc_data = {0u, 0u, 0u, 0u};
+    int32_t sc_slot = -1;
+    int sc_cw = 0, sc_which = 0;
+    if (tid < sc_units) {
+        const u32x4 *src;
+        int i;
+        sc_word(tid, src, i, sc_cw, sc_which);
+        sc_slot = a.slot_mapping[qs0 + i];
+        sc_data = *src;
+    }
+
     u32x4 qf[RT][KU4];
     int lim[RT];
 #pragma unroll
@@ -604,23 +632,20 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
         }
     }
 
-    // ---- fused scatter: the item holding the sequence's last keys (last
-    // row range, last key slice) copies this step's K/V rows of its KV
-    // head into their slots. No item of this launch reads those slots
-    // from the pool.
-    if (fused && (it.flags & PS_ITEM_WRITES_NEW)) {
-        constexpr int WPR = D * ELT / 16;   // 16-byte words per head row
-        const int n = ke - nc;
+    // ---- fused scatter: the stores (words past the first 64 NW come
+    // from a plain copy loop)
+    if (sc_units > 0) {
         u32x4 *pk = reinterpret_cast<u32x4 *>(const_cast<T *>(kp));
         u32x4 *pv = reinterpret_cast<u32x4 *>(const_cast<T *>(vp));
-        const int64_t rw = rs * ELT / 16;   // 16-byte words from one slot (or token) to the next
-        for (int w = tid; w < 2 * n * WPR; w += 64 * NW) {
-            const int which = w / (n * WPR), r2 = w - which * n * WPR;
-            const int i = r2 / WPR, cw = r2 - i * WPR;
+        if (tid < sc_units && (uint32_t)sc_slot < (uint32_t)a.num_slots)
+            (sc_which ? pv : pk)[(int64_t)sc_slot * rw16 + sc_cw] = sc_data;
+        for (int w = tid + 64 * NW; w < sc_units; w += 64 * NW) {
+            const u32x4 *src;
+            int i, cw, which;
+            sc_word(w, src, i, cw, which);
             const int32_t slot = a.slot_mapping[qs0 + i];
             if ((uint32_t)slot >= (uint32_t)a.num_slots) continue;
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(which ? vn : kn) + (int64_t)(nc + i) * rw;
-            (which ? pv : pk)[(int64_t)slot * rw + cw] = src[cw];
+            (which ? pv : pk)[(int64_t)slot * rw16 + cw] = *src;
         }
     }
 
