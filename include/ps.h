@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PS_ABI_VERSION 2
+#define PS_ABI_VERSION 3
 
 typedef int32_t ps_status;
 enum {
@@ -179,6 +179,13 @@ typedef struct {
     int64_t kv_bytes_unique;                    /* distinct physical K+V bytes read */
     int64_t q_bytes, out_bytes, scatter_bytes, table_bytes;
     double flops_decode, flops_prefill;
+    /* Shared prefixes: decode sequences whose tables open with the same
+     * blocks form groups; attention over a group's prefix runs once, in
+     * prefix_items prefill-kernel items (counted in prefill_items) whose
+     * rows come from every member, and merges with each member's own keys
+     * like a key split. step_fused: ps_step runs the scatter inside the
+     * attention launch. */
+    int32_t prefix_groups, prefix_items, step_fused, reserved;
 } ps_plan_info;
 
 ps_status ps_plan_get_info(const ps_plan *plan, ps_plan_info *info);

@@ -59,7 +59,8 @@ class ps_plan_info(ctypes.Structure):
         "decode_row_tiles")] + [(n, ctypes.c_int64) for n in (
         "kv_bytes_decode", "kv_bytes_prefill", "kv_bytes_unique", "q_bytes", "out_bytes",
         "scatter_bytes", "table_bytes")] + [("flops_decode", ctypes.c_double),
-                                            ("flops_prefill", ctypes.c_double)]
+                                            ("flops_prefill", ctypes.c_double)] + [
+        (n, ctypes.c_int32) for n in ("prefix_groups", "prefix_items", "step_fused", "reserved")]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -27,13 +27,28 @@ struct ps_item {
     // tile count): items that share prefix blocks then do not request the
     // same lines at the same time (softmax order is free). Prefill: 0.
     int32_t rot;
-    int32_t pad;
+    // Gathered items (PS_ITEM_GATHERED): which slice of the shared prefix's
+    // keys the item covers; its partials go to a row's dest + split * stride.
+    int32_t split;
 };
 static_assert(sizeof(ps_item) == 48, "ps_item layout");
 // The one item per (sequence, KV head) that holds the sequence's last keys
 // (last row range, last key slice): with the scatter fused into the
 // decode launch it writes the step's new K/V rows of its KV head.
 constexpr int32_t PS_ITEM_WRITES_NEW = 1;
+// A prefill-kernel item of the shared-prefix pass: its rows come from
+// several sequences, listed by the row map from entry partial_row on, and
+// every key of its range is visible to every row.
+constexpr int32_t PS_ITEM_GATHERED = 2;
+
+// One gathered row: which query row it reads and where its partial goes.
+struct ps_row {
+    int32_t q_row;   // t * num_q_heads + h: the row of q (and of out)
+    int32_t dest;    // workspace row of the first prefix slice's partial
+    int32_t stride;  // rows from one slice's partial to the next
+    int32_t pad;
+};
+static_assert(sizeof(ps_row) == 16, "ps_row layout");
 
 // A chunk of rows (at most ps_merge_rows(D)) of one set of split-K
 // partials, merged into the output by one workgroup of the merge kernel.
@@ -98,6 +113,7 @@ struct ps_attn_launch {
     const ps_item *prefill_items;
     const ps_merge *merges;
     const int32_t *decode_head;   // [n_decode][2 * PS_DEC_HEAD_TILES] block ids
+    const ps_row *row_map;        // rows of the gathered (shared-prefix) items
     float *ws_m;
     float *ws_l;
     float *ws_acc;

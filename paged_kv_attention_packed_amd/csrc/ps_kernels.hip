@@ -853,14 +853,34 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
     const int wr0 = it.row_begin + wave * RPW;
     const bool active = wr0 < it.row_end;
     const int wr_last = min(wr0 + RPW, it.row_end) - 1;
-    const int lim_lo = nc + div_g(a, wr0);      // smallest visibility limit among the wave's rows
-    const int lim_hi = nc + div_g(a, wr_last);  // largest
+    // A gathered item (shared-prefix pass) takes its rows from the row map;
+    // every key of its range is visible to all of them.
+    const bool gathered = (it.flags & PS_ITEM_GATHERED) != 0;
+    constexpr int kAllVisible = INT32_MAX / 2;
+    const int lim_lo = gathered ? kAllVisible : nc + div_g(a, wr0);      // smallest visibility limit among the wave's rows
+    const int lim_hi = gathered ? kAllVisible : nc + div_g(a, wr_last);  // largest
 
     u32x4 qf[RT][KU4];
     int lim[RT];
+    ps_row grow[RT];   // gathered rows' map entries
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-        load_q_row<DT, D>(a, wr0 + rt * 16 + c, it.row_end, g, j, qs0, nc, q4, qf[rt], lim[rt]);
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = wr0 + rt * 16 + c;
+        grow[rt] = ps_row{0, 0, 0, 0};
+        if (!gathered) {
+            load_q_row<DT, D>(a, r, it.row_end, g, j, qs0, nc, q4, qf[rt], lim[rt]);
+        } else if (r < it.row_end) {
+            grow[rt] = a.row_map[it.partial_row + r];
+            const T *qp = static_cast<const T *>(a.q) + (int64_t)grow[rt].q_row * D;
+#pragma unroll
+            for (int u = 0; u < KU4; ++u) qf[rt][u] = *reinterpret_cast<const u32x4 *>(qp + (u * 4 + q4) * (16 / ELT));
+            lim[rt] = kAllVisible;
+        } else {
+#pragma unroll
+            for (int u = 0; u < KU4; ++u) qf[rt][u] = u32x4{0u, 0u, 0u, 0u};
+            lim[rt] = -1;
+        }
+    }
 
     // Block ids of the item's key range go to LDS once: inside the ring
     // they could only be vector loads, and waiting for those would also
@@ -1078,13 +1098,14 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
         else l[rt] = xor_sum(l[rt]);
     }
 
-    if (it.partial_row >= 0) {
+    if (gathered || it.partial_row >= 0) {
         if (!active) return;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int r = wr0 + rt * 16 + c;
             if (r >= it.row_end) continue;
-            const int64_t pr = (int64_t)it.partial_row + (r - it.row_begin);
+            const int64_t pr = gathered ? (int64_t)grow[rt].dest + (int64_t)it.split * grow[rt].stride
+                                        : (int64_t)it.partial_row + (r - it.row_begin);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 if constexpr (ELT == 2) {  // tile t row 4q4 + i holds d = 16t + 4q4 + i

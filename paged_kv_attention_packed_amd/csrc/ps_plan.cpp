@@ -27,7 +27,8 @@ struct ps_plan {
     // the metadata blob, laid out exactly as it is copied to the device
     std::vector<uint8_t> blob;
     size_t off_qsl = 0, off_nc = 0, off_ctx = 0, off_slot = 0, off_pos = 0, off_bt = 0;
-    size_t off_dhead = 0;
+    size_t off_dhead = 0, off_rmap = 0;
+    int32_t n_gathered = 0;   // prefill items of the shared-prefix pass
     size_t off_dec = 0, off_pre = 0, off_mrg = 0;
     void *dev = nullptr;
     ps_plan_info info{};
@@ -51,6 +52,13 @@ int64_t env_int(const char *name, int64_t dflt) {
     char *end = nullptr;
     long long v = std::strtoll(s, &end, 10);
     return (end && *end == 0 && v > 0) ? (int64_t)v : dflt;
+}
+
+// A switch read from the environment: unset or empty gives dflt, "0" off.
+bool env_on(const char *name, bool dflt) {
+    const char *s = std::getenv(name);
+    if (!s || !*s) return dflt;
+    return std::strcmp(s, "0") != 0;
 }
 
 // Split [0, kmax) into near-equal pieces of about `target` keys, each a
@@ -172,19 +180,90 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
             is_dec[s] = (flags == PS_PLAN_ALL_DECODE) ||
                         (flags == PS_PLAN_DEFAULT && rows <= PS_DEC_MAX_ROWS);
         }
+        const int64_t pre_rows = ps_prefill_rows(pool->dtype);
+
+        // ---- shared prefixes. Decode sequences whose tables open with the
+        // same physical blocks (blocks shared by reference, PageServe "03
+        // Paged KV cache") form a group. Attention over the shared prefix
+        // then runs once per group, in prefill-kernel items whose query
+        // rows are gathered from every member: each prefix key lies below
+        // every member's first query position, so no mask applies. Each
+        // member's decode items cover only its keys after the prefix, and
+        // the partial softmax states merge like key splits. A member must
+        // share at least PS_CASCADE_MIN_KEYS tokens (whole blocks of its
+        // cached context) with the group's first sequence, and a group
+        // needs PS_CASCADE_MIN_SEQS members; PS_CASCADE=0 turns it off.
+        std::vector<int32_t> grp_of(S, -1);
+        std::vector<int32_t> grp_lead;
+        std::vector<int64_t> grp_keys;
+        std::vector<std::vector<int64_t>> grp_bounds;
+        if (flags == PS_PLAN_DEFAULT && env_on("PS_CASCADE", true)) {
+            const int64_t min_seqs = std::max<int64_t>(2, env_int("PS_CASCADE_MIN_SEQS", 8));
+            const int64_t min_blocks = ceil_div(std::max<int64_t>(16, env_int("PS_CASCADE_MIN_KEYS", 256)), PS_BLOCK);
+            // candidates, sorted by their first min_blocks block ids: runs of
+            // equal keys are the groups
+            std::vector<int32_t> cand;
+            for (int32_t s = 0; s < S; ++s)
+                if (is_dec[s] && num_computed_tokens[s] >= min_blocks * PS_BLOCK) cand.push_back(s);
+            auto row_of = [&](int32_t s) { return block_tables + (int64_t)s * block_table_stride; };
+            auto key_less = [&](int32_t x, int32_t y) {
+                const int32_t *a = row_of(x), *b = row_of(y);
+                for (int64_t i = 0; i < min_blocks; ++i)
+                    if (a[i] != b[i]) return a[i] < b[i];
+                return x < y;
+            };
+            auto key_same = [&](int32_t x, int32_t y) {
+                return std::memcmp(row_of(x), row_of(y), sizeof(int32_t) * (size_t)min_blocks) == 0;
+            };
+            std::sort(cand.begin(), cand.end(), key_less);
+            for (size_t a0 = 0; a0 < cand.size();) {
+                size_t a1 = a0 + 1;
+                while (a1 < cand.size() && key_same(cand[a0], cand[a1])) ++a1;
+                if ((int64_t)(a1 - a0) >= min_seqs) {
+                    // the group's prefix: the blocks every member shares with
+                    // the first one, within every member's cached context
+                    const int32_t lead = cand[a0];
+                    const int32_t *lrow = row_of(lead);
+                    int64_t common = num_computed_tokens[lead] / PS_BLOCK;
+                    for (size_t x = a0 + 1; x < a1; ++x) {
+                        const int32_t *mrow = row_of(cand[x]);
+                        const int64_t lim = std::min<int64_t>(common, num_computed_tokens[cand[x]] / PS_BLOCK);
+                        int64_t b = min_blocks;
+                        while (b < lim && mrow[b] == lrow[b]) ++b;
+                        common = b;
+                    }
+                    for (size_t x = a0; x < a1; ++x) grp_of[cand[x]] = (int32_t)grp_lead.size();
+                    grp_lead.push_back(lead);
+                    grp_keys.push_back(common * PS_BLOCK);
+                }
+                a0 = a1;
+            }
+            // prefix slices: about 128 prefix items per step (they share the
+            // launch with the decode items), none shorter than 256 keys
+            grp_bounds.resize(grp_lead.size());
+            for (size_t gi = 0; gi < grp_lead.size(); ++gi) {
+                int64_t rows = 0;
+                for (int32_t s = 0; s < S; ++s)
+                    if (grp_of[s] == (int32_t)gi) rows += (int64_t)g * q_lens[s];
+                const int64_t chunks = ceil_div(rows, pre_rows) * Hkv;
+                const int64_t want = std::max<int64_t>(1, std::min<int64_t>(ceil_div(128, chunks), grp_keys[gi] / 256));
+                const int64_t slice = env_int("PS_CASCADE_SLICE_KEYS", round_up(ceil_div(grp_keys[gi], want), PS_PRE_TILE));
+                key_splits(grp_keys[gi], std::max<int64_t>(PS_BLOCK, slice), PS_PRE_TILE, grp_bounds[gi]);
+            }
+        }
         // decode: a work item covers <= 32 packed rows and a slice of keys.
         // Slices are long (>= 2048 keys): a split costs a merge launch and
         // partial traffic, which only pays off against long contexts; very
         // long steps are cut into about 512 items (two per CU).
-        const int64_t pre_rows = ps_prefill_rows(pool->dtype);
         int64_t dec_keys = 0, pre_kmax = 0, pre_tiles = 0;
         for (int32_t s = 0; s < S; ++s) {
             const int64_t rows = (int64_t)g * q_lens[s], c = num_computed_tokens[s];
             const int64_t rb = is_dec[s] ? PS_DEC_MAX_ROWS : pre_rows;
+            const int64_t pk = grp_of[s] >= 0 ? grp_keys[grp_of[s]] : 0;
             for (int64_t r0 = 0; r0 < rows; r0 += rb) {
                 const int64_t r1 = std::min(rows, r0 + rb);
                 const int64_t kmax = c + (r1 - 1) / g + 1;
-                if (is_dec[s]) dec_keys += kmax * Hkv;
+                if (is_dec[s]) dec_keys += (kmax - pk) * Hkv;
                 else { pre_kmax = std::max(pre_kmax, kmax); pre_tiles += Hkv; }
             }
         }
@@ -209,19 +288,37 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         int64_t ws_rows = 0;
         int32_t dec_rt = 1;
         int32_t qs_run = 0;   // query_start_loc[s]
+        // gathered rows of each (group, KV head): the prefix items' row maps
+        std::vector<std::vector<ps_row>> grows(grp_lead.size() * (size_t)Hkv);
         for (int32_t s = 0; s < S; qs_run += q_lens[s], ++s) {
             const int64_t rows = (int64_t)g * q_lens[s], c = num_computed_tokens[s];
             const bool d = is_dec[s];
             const int64_t rb = d ? PS_DEC_MAX_ROWS : pre_rows;
+            const int32_t gi = grp_of[s];
+            const int64_t pk = gi >= 0 ? grp_keys[gi] : 0;                          // prefix keys
+            const int64_t npk = gi >= 0 ? (int64_t)grp_bounds[gi].size() - 1 : 0;   // prefix slices
             for (int32_t j = 0; j < Hkv; ++j) {
                 for (int64_t r0 = 0; r0 < rows; r0 += rb) {
                     const int64_t r1 = std::min(rows, r0 + rb);
                     const int64_t kmax = c + (r1 - 1) / g + 1;
-                    key_splits(kmax, d ? dec_split : std::min<int64_t>(pre_split, PS_PRE_MAX_KEYS),
+                    key_splits(kmax - pk, d ? dec_split : std::min<int64_t>(pre_split, PS_PRE_MAX_KEYS),
                                d ? PS_BLOCK : PS_PRE_TILE, bounds);
+                    for (int64_t &b : bounds) b += pk;
                     const int64_t ns = (int64_t)bounds.size() - 1;
+                    const int64_t nsplit = npk + ns;   // partial sets the merge combines
                     if (d) dec_rt = std::max<int32_t>(dec_rt, (int32_t)ceil_div(r1 - r0, 16));
-                    const int64_t base = ns > 1 ? ws_rows : -1;
+                    const int64_t base = nsplit > 1 ? ws_rows : -1;
+                    if (gi >= 0) {
+                        // the prefix slices' partials come first in the row range's block
+                        std::vector<ps_row> &gr = grows[(size_t)gi * Hkv + j];
+                        for (int64_t r = r0; r < r1; ++r) {
+                            ps_row e{};
+                            e.q_row = (int32_t)((qs_run + r / g) * num_q_heads + j * g + r % g);
+                            e.dest = (int32_t)(base + (r - r0));
+                            e.stride = (int32_t)(r1 - r0);
+                            gr.push_back(e);
+                        }
+                    }
                     for (int64_t i = 0; i < ns; ++i) {
                         ps_item it{};
                         it.seq = s;
@@ -230,7 +327,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                         it.row_end = (int32_t)r1;
                         it.key_begin = (int32_t)bounds[i];
                         it.key_end = (int32_t)bounds[i + 1];
-                        it.partial_row = ns > 1 ? (int32_t)(base + i * (r1 - r0)) : -1;
+                        it.partial_row = nsplit > 1 ? (int32_t)(base + (npk + i) * (r1 - r0)) : -1;
                         it.flags = r1 == rows && i == ns - 1 ? PS_ITEM_WRITES_NEW : 0;
                         it.q_start = qs_run;
                         it.num_computed = (int32_t)c;
@@ -240,7 +337,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                         }
                         (d ? dec : pre).push_back(it);
                     }
-                    if (ns > 1) {
+                    if (nsplit > 1) {
                         const int64_t mr = ps_merge_rows(D);
                         for (int64_t q0 = r0; q0 < r1; q0 += mr) {
                             ps_merge m{};
@@ -249,12 +346,39 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                             m.row_begin = (int32_t)q0;
                             m.row_end = (int32_t)std::min(r1, q0 + mr);
                             m.partial_row = (int32_t)(base + (q0 - r0));
-                            m.num_splits = (int32_t)ns;
+                            m.num_splits = (int32_t)nsplit;
                             m.split_stride = (int32_t)(r1 - r0);
                             m.q_start = qs_run;
                             mrg.push_back(m);
                         }
-                        ws_rows += ns * (r1 - r0);
+                        ws_rows += nsplit * (r1 - r0);
+                    }
+                }
+            }
+        }
+        // the prefix items: chunks of gathered rows x prefix key slices
+        std::vector<ps_row> rmap;
+        int32_t n_gathered = 0;
+        for (size_t gi = 0; gi < grp_lead.size(); ++gi) {
+            for (int32_t j = 0; j < Hkv; ++j) {
+                const std::vector<ps_row> &gr = grows[gi * Hkv + j];
+                for (size_t c0 = 0; c0 < gr.size(); c0 += (size_t)pre_rows) {
+                    const size_t c1 = std::min(gr.size(), c0 + (size_t)pre_rows);
+                    const int32_t off = (int32_t)rmap.size();
+                    rmap.insert(rmap.end(), gr.begin() + c0, gr.begin() + c1);
+                    for (size_t k = 0; k + 1 < grp_bounds[gi].size(); ++k) {
+                        ps_item it{};
+                        it.seq = grp_lead[gi];
+                        it.kv_head = j;
+                        it.row_begin = 0;
+                        it.row_end = (int32_t)(c1 - c0);
+                        it.key_begin = (int32_t)grp_bounds[gi][k];
+                        it.key_end = (int32_t)grp_bounds[gi][k + 1];
+                        it.partial_row = off;
+                        it.flags = PS_ITEM_GATHERED;
+                        it.split = (int32_t)k;
+                        pre.push_back(it);
+                        ++n_gathered;
                     }
                 }
             }
@@ -268,6 +392,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         p->n_dec = (int32_t)dec.size();
         p->n_pre = (int32_t)pre.size();
         p->n_mrg = (int32_t)mrg.size();
+        p->n_gathered = n_gathered;
 
         // ---- blob layout
         size_t off = 0;
@@ -286,6 +411,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         p->off_pre = take(sizeof(ps_item) * pre.size());
         p->off_mrg = take(sizeof(ps_merge) * mrg.size());
         p->off_dhead = take(sizeof(int32_t) * 2 * PS_DEC_HEAD_TILES * dec.size());
+        p->off_rmap = take(sizeof(ps_row) * rmap.size());
         p->blob.assign(off, 0);
 
         int32_t *qsl = p->host<int32_t>(p->off_qsl);
@@ -310,6 +436,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         if (!dec.empty()) std::memcpy(p->host<ps_item>(p->off_dec), dec.data(), sizeof(ps_item) * dec.size());
         if (!pre.empty()) std::memcpy(p->host<ps_item>(p->off_pre), pre.data(), sizeof(ps_item) * pre.size());
         if (!mrg.empty()) std::memcpy(p->host<ps_merge>(p->off_mrg), mrg.data(), sizeof(ps_merge) * mrg.size());
+        if (!rmap.empty()) std::memcpy(p->host<ps_row>(p->off_rmap), rmap.data(), sizeof(ps_row) * rmap.size());
         // decode items' first tiles in walk order: tile t covers keys
         // key_begin + 32 u .. +32, u = (t + rot) mod ntiles; a tile's second
         // block past key_end repeats the first (never read)
@@ -336,6 +463,9 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         I.dtype = pool->dtype;
         I.decode_items = p->n_dec;
         I.prefill_items = p->n_pre;
+        I.prefix_items = n_gathered;
+        I.prefix_groups = (int32_t)grp_lead.size();
+        I.step_fused = p->n_pre == n_gathered && p->n_dec > 0;
         I.merge_items = p->n_mrg;
         I.decode_row_tiles = dec_rt;
         const int64_t e = elt_bytes(pool->dtype);
@@ -479,6 +609,7 @@ static ps_status prepare_attention(const void *q, const ps_pool *pool, const int
     a.prefill_items = reinterpret_cast<const ps_item *>(dev + plan->off_pre);
     a.merges = reinterpret_cast<const ps_merge *>(dev + plan->off_mrg);
     a.decode_head = reinterpret_cast<const int32_t *>(dev + plan->off_dhead);
+    a.row_map = reinterpret_cast<const ps_row *>(dev + plan->off_rmap);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     a.ws_m = wl.bytes ? reinterpret_cast<float *>(ws + wl.off_m) : nullptr;
     a.ws_l = wl.bytes ? reinterpret_cast<float *>(ws + wl.off_l) : nullptr;
@@ -536,8 +667,10 @@ extern "C" ps_status ps_step(const void *q, const void *k, const void *v, const 
                                      num_q_heads, scale, plan, workspace, workspace_bytes, a, &empty);
     if (st != PS_OK || empty) return st;
     if (!k || !v || !slot_mapping) return ps_fail(PS_ERR_INVALID_ARGUMENT, "k, v or slot_mapping is NULL");
-    if (plan->n_pre == 0 && plan->n_dec > 0) {
-        // every sequence on the decode kernel: the scatter rides along
+    if (plan->n_pre == plan->n_gathered && plan->n_dec > 0) {
+        // every sequence on the decode kernel (shared-prefix items read
+        // only blocks below every member's new tokens): the scatter rides
+        // along
         a.fuse_scatter = 1;
         a.k_new = k;
         a.v_new = v;

@@ -158,9 +158,11 @@ def test_block_permutation_is_bit_invariant():
     assert torch.equal(oa, ob)
 
 
-def test_prefix_sharing_is_bit_invariant():
+def test_prefix_sharing_is_bit_invariant(monkeypatch):
     # the same logical contexts, once with the prefix in shared blocks and
-    # once with private copies of it
+    # once with private copies of it. Without the shared-prefix pass the
+    # physical sharing changes nothing, bit for bit; with it (the default)
+    # the shared step takes the prefix pass and both agree with the oracle.
     shared = workloads.build_step("shared", 41, "bf16", 12, 2, 128, 2048, [1] * 24 + [5] * 8,
                                   (np.arange(32) * 7 + 300).tolist(), prefix_tokens=256)
     private = workloads.build_step("private", 42, "bf16", 12, 2, 128, 2048, shared.q_lens,
@@ -171,8 +173,11 @@ def test_prefix_sharing_is_bit_invariant():
     assert len(np.unique(private.block_tables[:, 0])) == 32
     os_, _, _ = run_on_gpu(shared)
     op, _, _ = run_on_gpu(private)
-    assert torch.equal(os_, op)
     check_out(shared, os_)
+    check_out(private, op)
+    monkeypatch.setenv("PS_CASCADE", "0")
+    os0, _, _ = run_on_gpu(shared)
+    assert torch.equal(os0, op)
 
 
 def test_repeat_is_deterministic():

@@ -242,3 +242,42 @@ def test_split_plan_depends_only_on_logical_lengths():
     for key in ("decode_items", "prefill_items", "merge_items"):
         assert ia[key] == ib[key]
     assert P.ps_plan_sizes(pa)[1] == P.ps_plan_sizes(pb)[1]
+
+
+def test_shared_prefix_groups(monkeypatch):
+    # two groups (10 sequences sharing 320 tokens, 9 sharing 512) among
+    # sequences that share nothing, one of which shares only one block
+    st = workloads.prefix_groups_step(3, values=False)
+    g, hkv = st.num_q_heads // st.num_kv_heads, st.num_kv_heads
+    info = P.ps_plan_get_info(_plan(st))
+    assert info["prefix_groups"] == 2
+    assert info["prefill_items"] == info["prefix_items"] > 0
+    assert info["step_fused"] == 1
+    # one prefix pass per (group, KV head, chunk of <= 128 gathered rows, key slice)
+    assert info["prefix_items"] % hkv == 0
+    assert info["prefix_items"] >= hkv * (-(-10 * g // 128) + -(-9 * g // 128))
+    # every grouped sequence merges its own keys with the prefix pass
+    assert info["merge_items"] >= 19 * hkv
+
+    monkeypatch.setenv("PS_CASCADE", "0")
+    off = P.ps_plan_get_info(_plan(st))
+    assert off["prefix_groups"] == off["prefix_items"] == off["prefill_items"] == 0
+    assert off["decode_items"] == 24 * hkv and off["step_fused"] == 1
+    monkeypatch.delenv("PS_CASCADE")
+
+    monkeypatch.setenv("PS_CASCADE_MIN_SEQS", "10")   # group B has 9
+    assert P.ps_plan_get_info(_plan(st))["prefix_groups"] == 1
+    monkeypatch.setenv("PS_CASCADE_MIN_SEQS", "11")   # the outlier does not join group A
+    assert P.ps_plan_get_info(_plan(st))["prefix_groups"] == 0
+    monkeypatch.delenv("PS_CASCADE_MIN_SEQS")
+    monkeypatch.setenv("PS_CASCADE_MIN_KEYS", "336")  # group A shares 320 tokens
+    assert P.ps_plan_get_info(_plan(st))["prefix_groups"] == 1
+    monkeypatch.delenv("PS_CASCADE_MIN_KEYS")
+
+    for flags in (P.PS_PLAN_ALL_DECODE, P.PS_PLAN_ALL_PREFILL):
+        assert P.ps_plan_get_info(_plan(st, flags))["prefix_groups"] == 0
+    # a chunk in the step: the scatter is no longer fused
+    wp = workloads.prefix_groups_step(3, with_prefill=True, values=False)
+    iw = P.ps_plan_get_info(_plan(wp))
+    assert iw["prefix_groups"] == 2 and iw["step_fused"] == 0
+    assert iw["prefill_items"] > iw["prefix_items"]

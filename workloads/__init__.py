@@ -31,7 +31,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Optional, Sequence
+from typing import Optional, Sequence, Tuple
 
 import numpy as np
 import torch
@@ -95,13 +95,21 @@ def build_step(name: str, seed: int, dtype, num_q_heads: int, num_kv_heads: int,
                num_computed: Sequence[int], *, rng: Optional[np.random.Generator] = None,
                prefix_tokens: int = 0, num_layers: int = 1, layer: int = 0,
                scale: Optional[float] = None, values: bool = True,
-               table_width: Optional[int] = None) -> Step:
+               table_width: Optional[int] = None,
+               groups: Optional[Sequence[Tuple[Sequence[int], int]]] = None) -> Step:
     """Draw block tables and values for the given lengths.
 
     ``rng`` continues a generator that already drew the lengths; when None a
     fresh one is seeded with ``seed``. ``prefix_tokens`` (a multiple of 16)
     gives every sequence the same first blocks and the same values there.
+    ``groups`` instead lists (members, prefix_tokens) pairs: the members of
+    a pair share their first prefix_tokens / 16 blocks and the values there
+    (disjoint member lists; sequences in no pair share nothing).
     """
+    if groups is not None:
+        return _build_grouped(name, seed, dtype, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                              q_lens, num_computed, groups, rng=rng, num_layers=num_layers,
+                              layer=layer, scale=scale, values=values)
     if isinstance(dtype, str):
         dtype = _DTYPES[dtype]
     if rng is None:
@@ -160,6 +168,113 @@ def build_step(name: str, seed: int, dtype, num_q_heads: int, num_kv_heads: int,
                 q_lens=q_lens, num_computed=num_computed, block_tables=tables,
                 prefix_blocks=prefix_blocks, k_ctx=k_ctx, v_ctx=v_ctx, k=k, v=v, q=q,
                 scale=float(scale))
+
+
+def _build_grouped(name, seed, dtype, num_q_heads, num_kv_heads, head_dim, num_blocks, q_lens,
+                   num_computed, groups, *, rng=None, num_layers=1, layer=0, scale=None,
+                   values=True) -> Step:
+    """build_step with several shared-prefix groups (see its ``groups``)."""
+    if isinstance(dtype, str):
+        dtype = _DTYPES[dtype]
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    num_computed = np.asarray(num_computed, dtype=np.int32)
+    S = len(q_lens)
+    ctx = num_computed.astype(np.int64) + q_lens
+    nblk = [(int(c) + BLOCK_SIZE - 1) // BLOCK_SIZE for c in ctx]
+    group_of = [-1] * S
+    for gi, (members, ptok) in enumerate(groups):
+        assert ptok % BLOCK_SIZE == 0
+        for m in members:
+            assert group_of[m] < 0, "a sequence in two groups"
+            assert num_computed[m] >= ptok, "prefix must lie in the cached context"
+            group_of[m] = gi
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    off = 0
+    gblocks = []
+    for members, ptok in groups:
+        gblocks.append(perm[off:off + ptok // BLOCK_SIZE])
+        off += ptok // BLOCK_SIZE
+    tables = np.full((S, max(max(nblk) if S else 1, 1)), -1, dtype=np.int32)
+    for s in range(S):
+        pb = len(gblocks[group_of[s]]) if group_of[s] >= 0 else 0
+        if pb:
+            tables[s, :pb] = gblocks[group_of[s]]
+        own = nblk[s] - pb
+        tables[s, pb:nblk[s]] = perm[off:off + own]
+        off += own
+    assert off <= num_blocks, f"{name}: needs {off} blocks, pool has {num_blocks}"
+    k_ctx = v_ctx = k = v = q = None
+    T = int(q_lens.sum())
+    if values:
+        gk = [_normal(rng, (ptok, num_kv_heads, head_dim), dtype) for _, ptok in groups]
+        gv = [_normal(rng, (ptok, num_kv_heads, head_dim), dtype) for _, ptok in groups]
+        ks, vs = [], []
+        for s in range(S):
+            gi = group_of[s]
+            ptok = groups[gi][1] if gi >= 0 else 0
+            rest = int(num_computed[s]) - ptok
+            pk = gk[gi] if gi >= 0 else _normal(rng, (0, num_kv_heads, head_dim), dtype)
+            pv = gv[gi] if gi >= 0 else _normal(rng, (0, num_kv_heads, head_dim), dtype)
+            ks.append(torch.cat([pk, _normal(rng, (rest, num_kv_heads, head_dim), dtype)]))
+            vs.append(torch.cat([pv, _normal(rng, (rest, num_kv_heads, head_dim), dtype)]))
+        k_ctx = torch.cat(ks)
+        v_ctx = torch.cat(vs)
+        k = _normal(rng, (T, num_kv_heads, head_dim), dtype)
+        v = _normal(rng, (T, num_kv_heads, head_dim), dtype)
+        q = _normal(rng, (T, num_q_heads, head_dim), dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return Step(name=name, seed=seed, dtype=dtype, num_q_heads=num_q_heads,
+                num_kv_heads=num_kv_heads, head_dim=head_dim, num_blocks=num_blocks,
+                num_layers=num_layers, layer=layer, block_size=BLOCK_SIZE,
+                q_lens=q_lens, num_computed=num_computed, block_tables=tables,
+                prefix_blocks=0, k_ctx=k_ctx, v_ctx=v_ctx, k=k, v=v, q=q, scale=float(scale))
+
+
+def prefix_groups_step(seed: int, dtype="f16", num_q_heads: int = 14, num_kv_heads: int = 2,
+                       head_dim: int = 64, verify: bool = False, with_prefill: bool = False,
+                       values: bool = True) -> Step:
+    """A decode step with two shared-prefix groups among other sequences.
+
+    Group A: 10 sequences sharing 320 tokens (20 blocks); group B: 9
+    sharing 512 tokens, some of them with nothing cached past the prefix.
+    Four sequences share nothing, and one more shares only group A's first
+    block (too little to join it). ``verify`` gives group B 2-5 query
+    tokens per sequence; ``with_prefill`` adds a 40-token chunk. Sequences
+    of the groups are interleaved with the others in the packed order.
+    """
+    rng = np.random.default_rng(seed)
+    a_n = 1 + (rng.integers(0, 3, size=10) if verify else np.zeros(10, dtype=np.int64))
+    a_c = 320 + rng.integers(0, 100, size=10, endpoint=True)
+    b_n = rng.integers(2, 5, size=9, endpoint=True) if verify else np.ones(9, dtype=np.int64)
+    b_c = 512 + np.where(np.arange(9) % 3 == 0, 0, rng.integers(1, 64, size=9, endpoint=True))
+    l_n = np.ones(5, dtype=np.int64)
+    l_c = rng.integers(10, 300, size=5, endpoint=True)
+    l_c[4] = 400   # the outlier
+    q_lens = list(a_n) + list(b_n) + list(l_n)
+    num_computed = list(a_c) + list(b_c) + list(l_c)
+    if with_prefill:
+        q_lens.append(40)
+        num_computed.append(30)
+    S = len(q_lens)
+    order = rng.permutation(S)                      # packed position of each sequence
+    inv = np.empty(S, dtype=np.int64)
+    inv[order] = np.arange(S)
+    q_lens = [int(q_lens[i]) for i in order]
+    num_computed = [int(num_computed[i]) for i in order]
+    groups = [([int(inv[i]) for i in range(10)], 320), ([int(inv[i]) for i in range(10, 19)], 512)]
+    st = build_step("prefix-groups", seed, dtype, num_q_heads, num_kv_heads, head_dim, 512,
+                    q_lens, num_computed, rng=rng, values=values, groups=groups)
+    # the outlier takes group A's first block, and its values
+    o, a0 = int(inv[23]), groups[0][0][0]
+    st.block_tables[o, 0] = st.block_tables[a0, 0]
+    if values:
+        offs = np.concatenate([[0], np.cumsum(st.num_computed.astype(np.int64))])
+        for t in (st.k_ctx, st.v_ctx):
+            t[offs[o]:offs[o] + BLOCK_SIZE] = t[offs[a0]:offs[a0] + BLOCK_SIZE]
+    return st
 
 
 # ---------------------------------------------------------------------------
