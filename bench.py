@@ -477,9 +477,10 @@ def main():
     torch.cuda.synchronize()
     ms_scatter = e0.elapsed_time(e1) / args.steps
 
-    # ---- the step call alone, eager: with every sequence on the decode
-    # kernel ps_step is one fused launch (attention + scatter)
-    fused = info["prefill_items"] == 0 and info["decode_items"] > 0
+    # ---- the step call alone, eager: when the planner fuses the scatter
+    # into the attention launch (every non-prefix item on the decode
+    # kernel), ps_step is that one launch (plus the split-K merge)
+    fused = info["step_fused"] == 1
     e0.record(stream)
     for i in range(args.steps):
         ps.step(q, k, v, pools[i % nrot], outs[i % len(outs)], step.scale, stream)
@@ -517,8 +518,10 @@ def main():
     mixed = (nd > 0 and npf > 0 and step.dtype_name != "f32"
              and os.environ.get("PS_MIXED", "1") != "0"
              and os.environ.get("PS_PREFILL_VARIANT", "0") == "0")
+    npx = info["prefix_items"]
+    pre_note = f"{npf} prefill items, {npx} of them shared-prefix" if npx else f"{npf} prefill items"
     if mixed:
-        kernels = [f"ps_mixed_kernel x{nd + npf} ({nd} decode + {npf} prefill items)"]
+        kernels = [f"ps_mixed_kernel x{nd + npf} ({nd} decode + {pre_note})"]
     else:
         kernels = ([f"ps_decode_kernel x{nd}"] if nd else []) + \
                   ([f"ps_prefill_kernel x{npf}"] if npf else [])
@@ -529,7 +532,7 @@ def main():
     # (fp32 rows run v_mfma_f32_16x16x4f32, priced at the fp32 matrix peak)
     mfma_peak = MFMA_PEAK_TFLOPS if step.dtype_name != "f32" else FP32_PEAK_TFLOPS
     t_hbm = dom_bytes / (HBM_PEAK_GBS * 1e9)
-    dom_flops = flops if not fused else info["flops_decode"]
+    dom_flops = flops
     t_mfma = dom_flops / (mfma_peak * 1e12)
     hbm_line = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
