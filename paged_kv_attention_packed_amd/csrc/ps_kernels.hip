@@ -328,6 +328,43 @@ __global__ __launch_bounds__(256) void ps_copy_blocks_kernel(const u32x4 *__rest
 // the slice round-robin, each double-buffering the next tile's K/V in
 // registers, then merge their softmax states through LDS.
 
+// one 16-byte global -> LDS DMA per lane; lane l lands at lds + 16 * l
+// Issued as inline asm: the compiler cannot tell which LDS bytes a DMA in
+// flight will write, so for the builtin (or an asm that clobbers memory) it
+// waits for every DMA in flight, the next tiles' too, before each LDS read.
+// Ordering is explicit instead: wait_vmcnt for this thread's DMAs, then
+// lds_barrier (whose asm does clobber memory) for everyone's. m0 holds the
+// LDS destination; nothing else on gfx950 reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is a reserved register: the clobber is the point
+__device__ inline void dma16(const void *src, uint8_t *lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t off = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(off) : "m0");
+#endif
+}
+// Same, addressed as a scalar base plus a 32-bit per-lane byte offset.
+__device__ inline void dma16_sv(const void *base, uint32_t voff, uint32_t lds_off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_off) : "m0");
+#endif
+}
+#pragma clang diagnostic pop
+
+// 16-byte chunk position of `chunk` in key row `row`: XOR-swizzled so that
+// 16 consecutive lanes reading one chunk of 16 consecutive rows, or 16
+// chunks of one row, touch 16 different 16-byte bank groups (256 bytes)
+//
+// 256-byte (and longer) rows: chunk ^ f(row), f a bijection of row % 16
+// that is even for each aligned group of 4 rows, so the transposed V reads
+// (2 adjacent chunks of 4 adjacent rows) also land in 8 distinct groups.
+template <int ROWB>
+__device__ inline int swz(int chunk, int row) {
+    if constexpr (ROWB >= 256) return chunk ^ (((row & 7) << 1) | ((row >> 3) & 1));
+    else return chunk ^ ((row >> 1) & 7);  // 128-byte rows: two rows share 256 bytes
+}
+
 // NW waves per workgroup: more waves cover a short key slice in one round
 // trip (each wave takes every NW-th 32-key tile); the register budget
 // allows 2 waves per SIMD up to 8 waves and 4 per SIMD at 16.
@@ -611,11 +648,103 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
             if (tid + i * 64 * NW < nb) sbt[tid + i * 64 * NW] = stg[i];
         lds_barrier();
     }
-    if constexpr (!DOUBLE_BUFFER) {
-        // two row tiles leave no registers for a second tile in flight;
+    // Two row tiles of 16-bit rows of 128 leave no registers for a second
+    // tile in flight. Their wave's region of the LDS merge buffer (idle
+    // until the wave's last tile, 16 KiB: K and V of one tile) takes it
+    // instead: tile ti + NW is DMA'd there while tile ti is computed, then
+    // read into the registers. Rows sit as in the prefill ring (16-byte
+    // chunks XOR-swizzled by row), so the fragment reads are conflict free.
+    constexpr bool LDS_SLOT = !DOUBLE_BUFFER && ELT == 2 && D == 128;
+    static_assert(!LDS_SLOT || sizeof(sh.o[0]) == 2 * PS_DEC_TILE * D * ELT, "slot size");
+    uint8_t *const slot = reinterpret_cast<uint8_t *>(&sh.o[wave][0][0]);
+    const uint32_t slot_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)slot;
+    // DMA of the tile at k0 (blocks b0, b1): instruction i moves rows
+    // 4 (i % 8) .. +3 of K (i < 8) or V, lane l row + l / 16, position l % 16
+    auto dma_tile = [&](int k0, int64_t b0, int64_t b1) {
+        const int p = lane & 15;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int kv = i >> 3;
+            const int rr = (i & 7) * 4 + (lane >> 4);       // row of the tile
+            const int64_t blk = (i & 7) >= 4 ? b1 : b0;      // compile-time choice
+            const int chunk = swz<D * ELT>(p, rr) * (16 / ELT);
+            const T *pool = kv ? vp : kp;
+            if (k0 + PS_DEC_TILE <= new_lo) {
+                // the block base is wave-uniform; say so, for the scalar operand
+                const uint64_t base = (uint64_t)(uintptr_t)(pool + blk * 16 * rs);
+                // (readfirstlane returns int: widen through uint32_t, or the
+                // low half would sign-extend over the high one)
+                const uint64_t ubase =
+                    ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
+                    (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
+                dma16_sv(reinterpret_cast<const void *>(ubase), (uint32_t)(((rr & 15) * (int)rs + chunk) * ELT),
+                         slot_lds + i * 1024);
+            } else {
+                const int pos = k0 + rr;
+                const T *src = pos >= new_lo && pos < ke ? (kv ? vn : kn) + (int64_t)pos * rs + chunk
+                                                         : pool + (blk * 16 + (rr & 15)) * rs + chunk;
+                dma16(src, slot + i * 1024);
+            }
+        }
+    };
+    // the slot's tile into the registers of buffer 0, as load_tile leaves them
+    auto read_slot = [&]() {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int r = sb * 16 + c;
+#pragma unroll
+            for (int u = 0; u < KU4; ++u)
+                kf[0][sb][u] = *reinterpret_cast<const u32x4 *>(slot + r * (D * ELT) +
+                                                                swz<D * ELT>(u * 4 + q4, r) * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rv = sb * 16 + 4 * q4 + i;
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(slot + PS_DEC_TILE * (D * ELT) +
+                                                                 rv * (D * ELT) + swz<D * ELT>(c, rv) * 16);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) vr[0][sb * 4 + i][w] = x[w];
+            }
+        }
+    };
+    if constexpr (!DOUBLE_BUFFER && !LDS_SLOT) {
         // the other resident waves cover the load latency
         for (; ti < ntiles; ti += NW) {
             if (ti != wave) load_tile(B0{}, ti, key0(ti), FromLds{});
+            compute_tile(B0{}, key0(ti));
+        }
+    }
+    if constexpr (LDS_SLOT) {
+        if (ti + NW < ntiles) {
+            // the wave's second tile: ids from the head (or the table)
+            const int t1 = ti + NW, k1 = key0(t1);
+            int64_t b0, b1;
+            if (t1 < PS_DEC_HEAD_TILES) {
+                b0 = hid1.x;
+                b1 = hid1.y;
+            } else {
+                b0 = bt[k1 >> 4];
+                b1 = k1 + 16 < ke ? (int64_t)bt[(k1 >> 4) + 1] : b0;
+            }
+            dma_tile(k1, b0, b1);
+        }
+        for (; ti < ntiles; ti += NW) {
+            if (ti != wave) {
+                // the DMA of this tile (the only vector memory operation in
+                // flight) has landed; the asm fences keep the compiler from
+                // moving LDS reads across the waits
+                wait_vmcnt<0>();
+                asm volatile("" ::: "memory");
+                read_slot();
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot is read
+                asm volatile("" ::: "memory");
+                if (ti + NW < ntiles) {
+                    const int kn2 = key0(ti + NW);
+                    const int li = (kn2 - kb) >> 4;
+                    const int64_t b0 = __builtin_amdgcn_readfirstlane(sbt[li]);
+                    const int64_t b1 = kn2 + 16 < ke ? (int64_t)__builtin_amdgcn_readfirstlane(sbt[li + 1]) : b0;
+                    dma_tile(kn2, b0, b1);
+                }
+            }
             compute_tile(B0{}, key0(ti));
         }
     }
@@ -729,42 +858,6 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
 // lines). Hand-offs use a bare s_barrier with explicit s_waitcnt, since a
 // fenced barrier would also wait for the tile still in flight.
 
-// one 16-byte global -> LDS DMA per lane; lane l lands at lds + 16 * l
-// Issued as inline asm: the compiler cannot tell which LDS bytes a DMA in
-// flight will write, so for the builtin (or an asm that clobbers memory) it
-// waits for every DMA in flight, the next tiles' too, before each LDS read.
-// Ordering is explicit instead: wait_vmcnt for this thread's DMAs, then
-// lds_barrier (whose asm does clobber memory) for everyone's. m0 holds the
-// LDS destination; nothing else on gfx950 reads it.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is a reserved register: the clobber is the point
-__device__ inline void dma16(const void *src, uint8_t *lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t off = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(off) : "m0");
-#endif
-}
-// Same, addressed as a scalar base plus a 32-bit per-lane byte offset.
-__device__ inline void dma16_sv(const void *base, uint32_t voff, uint32_t lds_off) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_off) : "m0");
-#endif
-}
-#pragma clang diagnostic pop
-
-// 16-byte chunk position of `chunk` in key row `row`: XOR-swizzled so that
-// 16 consecutive lanes reading one chunk of 16 consecutive rows, or 16
-// chunks of one row, touch 16 different 16-byte bank groups (256 bytes)
-//
-// 256-byte (and longer) rows: chunk ^ f(row), f a bijection of row % 16
-// that is even for each aligned group of 4 rows, so the transposed V reads
-// (2 adjacent chunks of 4 adjacent rows) also land in 8 distinct groups.
-template <int ROWB>
-__device__ inline int swz(int chunk, int row) {
-    if constexpr (ROWB >= 256) return chunk ^ (((row & 7) << 1) | ((row >> 3) & 1));
-    else return chunk ^ ((row >> 1) & 7);  // 128-byte rows: two rows share 256 bytes
-}
 
 // 4 16-bit values per lane, transposed within each 16-lane group: lane i
 // receives element i % 4 of the 8-byte loads issued by lanes 4e + i / 4,
