@@ -270,3 +270,23 @@ def test_step_entry_fused_with_splits_and_row_ranges(split, monkeypatch):
         _note(f"fused split={split} {dt} D={d} q_lens={st.q_lens.tolist()}")
         out = _same_as_separate_calls(st, P.PS_PLAN_ALL_DECODE)
         check_out(st, out)
+
+
+@pytest.mark.parametrize("case", [("bf16", 12, 2, 128), ("f16", 12, 2, 128), ("f16", 24, 2, 128)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_verify_rows_long_contexts_fused(case):
+    # verify rows filling two 16-row tiles per work item against contexts of
+    # many 32-key tiles per wave: the second tile in flight goes through the
+    # LDS, including the tile that holds this step's keys (read from k / v)
+    dt, hq, hkv, d = case
+    g = hq // hkv
+    rng = np.random.default_rng(700 + hq)
+    S = 12
+    q_lens = rng.integers(max(2, 17 // g + 1), 32 // g, size=S, endpoint=True)
+    ctx = rng.integers(300, 2000, size=S, endpoint=True)
+    st = workloads.build_step("verify-long", 700 + hq, dt, hq, hkv, d, 2048, q_lens.tolist(),
+                              (ctx - q_lens).tolist(), rng=rng)
+    assert all(g * n > 16 for n in st.q_lens.tolist())
+    _note(f"verify-long {case} q_lens={st.q_lens.tolist()}")
+    out = _same_as_separate_calls(st, P.PS_PLAN_DEFAULT)
+    check_out(st, out)
