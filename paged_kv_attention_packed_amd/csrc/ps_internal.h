@@ -209,6 +209,7 @@ int ps_launch_scatter(const void *k, const void *v, const int32_t *slot_mapping,
                       int32_t num_tokens, const ps_pool *pool, void *stream);
 int ps_launch_attention(const ps_attn_launch &a, void *stream);
 int ps_prefill_rows(int dtype);  // packed rows per prefill work item
+bool ps_mixed_launch(int dtype);  // decode and prefill items share one launch
 int ps_launch_copy_blocks(const ps_pool *src, const ps_pool *dst, const int32_t *src_blocks,
                           const int32_t *dst_blocks, int32_t num_pairs, void *stream);
 int ps_launch_rope_cache(const ps_rope_launch &a, void *stream);

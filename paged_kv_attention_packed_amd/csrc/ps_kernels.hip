@@ -1350,6 +1350,16 @@ int ps_prefill_rows(int dtype) {
 }
 
 namespace psk {
+bool mixed_launch();
+}
+
+// Whether a step of this dtype with both decode and prefill items runs them
+// in one launch (the planner sizes prefill key slices for it).
+bool ps_mixed_launch(int dtype) {
+    return dtype != PS_F32 && psk::prefill_variant() == 0 && psk::mixed_launch();
+}
+
+namespace psk {
 
 // Decode and prefill items in one launch when a step has both (tuning knob,
 // PS_MIXED=0 launches them one after the other).

@@ -279,10 +279,20 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         // than ~512 keys costs more in partials (a 128-row tile's partials
         // weigh as much as ~500 keys of K/V) than it balances.
         const int64_t pre_slices = std::max<int64_t>(1, 1536 / std::max<int64_t>(1, pre_tiles));
-        const int64_t pre_split = env_int(
-            "PS_PREFILL_SPLIT",
-            pre_tiles >= 512 ? INT32_MAX
-                             : std::max<int64_t>(512, round_up(ceil_div(pre_kmax, pre_slices), PS_PRE_TILE)));
+        int64_t pre_auto = pre_tiles >= 512 ? INT32_MAX
+                                            : std::max<int64_t>(512, round_up(ceil_div(pre_kmax, pre_slices), PS_PRE_TILE));
+        // In a mixed launch the decode items keep the chip busy while the
+        // prefill items run. Slicing then pays only if an unsliced prefill
+        // item would outlast the decode work by far: it costs a merge
+        // launch and the partials. Time models measured on MI355X: a
+        // 128-row prefill item at ~1.9 TFLOP/s (two per CU), decode K/V
+        // reads at ~4 TB/s.
+        if (dec_keys > 0 && ps_mixed_launch(pool->dtype)) {
+            const double t_dec = (double)dec_keys * 2.0 * D * elt_bytes(pool->dtype) / 4.0e6;  // us
+            const double t_pre = (double)pre_kmax * pre_rows * 4.0 * D / 1.9e6;               // us
+            if (t_pre <= 2.0 * t_dec) pre_auto = INT32_MAX;
+        }
+        const int64_t pre_split = env_int("PS_PREFILL_SPLIT", pre_auto);
 
         std::vector<int64_t> bounds;
         int64_t ws_rows = 0;
