@@ -20,10 +20,13 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("case", ["decode-fp16", "mixed-bf16", "split-bf16"])
+@pytest.mark.parametrize("case", ["decode-fp16", "mixed-bf16", "split-bf16", "prefix-bf16"])
 def test_graph_replay_matches_eager(case, monkeypatch):
     if case == "decode-fp16":
         st = workloads.config(2)
+    elif case == "prefix-bf16":  # shared-prefix pass, merges and the fused scatter
+        st = workloads.prefix_groups_step(31, dtype="bf16", num_q_heads=12, num_kv_heads=2, head_dim=128,
+                                          verify=True)
     elif case == "mixed-bf16":
         st = workloads.random_step(77, dtype="bf16", num_seqs=8, max_q=80, max_ctx=600)
     else:  # force split-K partials and the merge kernel into the graph
