@@ -1052,6 +1052,33 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
             for (int rt = 0; rt < RT; ++rt) sacc[rt][sb] = qk_tile<DT, D>(kf, qf[rt]);
         }
         __builtin_amdgcn_s_setprio(0);
+        // 16-bit data: the V operands of the first 32-key half are read
+        // here, ahead of the softmax (they do not depend on P), so that
+        // their LDS latency hides under its VALU work; the softmax's
+        // rescale branch keeps the compiler from sinking them to their use.
+        // A operand of O^T tile t straight from LDS with transposing reads:
+        // lane (c, q4) gets V[keys 4q4..4q4+3 and 16+4q4..19+4q4][d = 16t +
+        // c]; in the group the source lane j reads row (j / 4) of the key
+        // quad, d quad (j % 4).
+        const int j16 = lane & 15;
+        const int vtrow = 4 * q4 + (j16 >> 2);
+        const int tbyte = (j16 & 3) * 8;  // within a 32-byte d tile
+        auto v_half = [&](int h, u32x4 (&av)[NT]) {
+            const int r0 = 32 * h + vtrow, r1 = r0 + 16;
+            const uint8_t *v0 = vsm + r0 * ROWB, *v1 = vsm + r1 * ROWB;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int b = t * 32 + tbyte;
+                const u32x2 lo = lds_read_tr16(v0 + swz<ROWB>(b >> 4, r0) * 16 + (b & 15));
+                const u32x2 hi = lds_read_tr16(v1 + swz<ROWB>(b >> 4, r1) * 16 + (b & 15));
+                av[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+        };
+        u32x4 av0[ELT == 2 ? NT : 1];
+        if constexpr (ELT == 2) {
+            // (V rows past key_end were zeroed in LDS before this tile)
+            v_half(0, av0);
+        }
         float pv[RT][4 * NSB];
         if (full) {  // (wave-uniform) every key of the tile is visible to every row
 #pragma unroll
@@ -1075,14 +1102,6 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
         __builtin_amdgcn_s_setprio(1);
         // P.V over 32-key halves
         if constexpr (ELT == 2) {
-            // A operand of O^T tile t straight from LDS with transposing
-            // reads: lane (c, q4) gets V[keys 4q4..4q4+3 and 16+4q4..19+4q4][d =
-            // 16t + c]; in the group the source lane j reads row (j / 4) of
-            // the key quad, d quad (j % 4)
-            const int j16 = lane & 15;
-            const int trow = 4 * q4 + (j16 >> 2);
-            const int tbyte = (j16 & 3) * 8;  // within a 32-byte d tile
-            // (V rows past key_end were zeroed in LDS before this tile)
 #pragma unroll
             for (int h = 0; h < NSB / 2; ++h) {
                 u32x4 pb[RT];
@@ -1091,16 +1110,17 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         pb[rt][e] = pack2(pv[rt][8 * h + 2 * e], pv[rt][8 * h + 2 * e + 1], DT{});
-                const int r0 = 32 * h + trow, r1 = r0 + 16;
-                const uint8_t *v0 = vsm + r0 * ROWB, *v1 = vsm + r1 * ROWB;
+                u32x4 av[NT];
+                if (h == 0) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) av[t] = av0[t];
+                } else {
+                    v_half(h, av);
+                }
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const int b = t * 32 + tbyte;
-                    const u32x2 lo = lds_read_tr16(v0 + swz<ROWB>(b >> 4, r0) * 16 + (b & 15));
-                    const u32x2 hi = lds_read_tr16(v1 + swz<ROWB>(b >> 4, r1) * 16 + (b & 15));
-                    const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) o[rt][t] = mfma32(av, pb[rt], o[rt][t], DT{});
+                    for (int rt = 0; rt < RT; ++rt) o[rt][t] = mfma32(av[t], pb[rt], o[rt][t], DT{});
                 }
                 constexpr uint32_t one2 = std::is_same<DT, TBF16>::value ? 0x3F803F80u : 0x3C003C00u;
                 const u32x4 ones = {one2, one2, one2, one2};
