@@ -240,23 +240,25 @@ __device__ inline int div_g(const ps_attn_launch &a, int r) {
 
 // Which query row a lane's packed row stands for, its visibility limit and
 // its Q fragment.
+// A row past the item's end (r >= row_end) loads the item's last row
+// instead and gets lim = -1: where its keys are masked it sees none, where
+// they are not its results are finite and never stored. Loading it
+// unconditionally keeps the loads out of a branch whose other side would
+// write the same registers, which would make the compiler wait for them
+// (and for everything issued before them) on the spot.
 template <class DT, int D>
 __device__ inline void load_q_row(const ps_attn_launch &a, int r, int row_end, int g, int kv_head,
                                   int qs0, int nc, int q4, u32x4 (&qf)[Geo<DT, D>::KU4], int &lim) {
-    if (r < row_end) {
-        const int tok = div_g(a, r);
-        const int h = kv_head * g + (r - tok * g);
-        lim = nc + tok;
-        const typename DT::T *qp =
-            static_cast<const typename DT::T *>(a.q) + ((int64_t)(qs0 + tok) * a.num_q_heads + h) * D;
+    const bool ok = r < row_end;
+    const int rr = ok ? r : row_end - 1;
+    const int tok = div_g(a, rr);
+    const int h = kv_head * g + (rr - tok * g);
+    lim = ok ? nc + tok : -1;
+    const typename DT::T *qp =
+        static_cast<const typename DT::T *>(a.q) + ((int64_t)(qs0 + tok) * a.num_q_heads + h) * D;
 #pragma unroll
-        for (int u = 0; u < Geo<DT, D>::KU4; ++u)
-            qf[u] = *reinterpret_cast<const u32x4 *>(qp + (u * 4 + q4) * (16 / DT::ELT));
-    } else {
-        lim = -1;
-#pragma unroll
-        for (int u = 0; u < Geo<DT, D>::KU4; ++u) qf[u] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int u = 0; u < Geo<DT, D>::KU4; ++u)
+        qf[u] = *reinterpret_cast<const u32x4 *>(qp + (u * 4 + q4) * (16 / DT::ELT));
 }
 
 // ---------------------------------------------------------------------------
@@ -953,34 +955,6 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
     const int lim_lo = gathered ? kAllVisible : nc + div_g(a, wr0);      // smallest visibility limit among the wave's rows
     const int lim_hi = gathered ? kAllVisible : nc + div_g(a, wr_last);  // largest
 
-    u32x4 qf[RT][KU4];
-    int lim[RT];
-    ps_row grow[RT];   // gathered rows' map entries
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int r = wr0 + rt * 16 + c;
-        grow[rt] = ps_row{0, 0, 0, 0};
-        if (!gathered) {
-            load_q_row<DT, D>(a, r, it.row_end, g, j, qs0, nc, q4, qf[rt], lim[rt]);
-        } else if (r < it.row_end) {
-            grow[rt] = a.row_map[it.partial_row + r];
-            const T *qp = static_cast<const T *>(a.q) + (int64_t)grow[rt].q_row * D;
-#pragma unroll
-            for (int u = 0; u < KU4; ++u) qf[rt][u] = *reinterpret_cast<const u32x4 *>(qp + (u * 4 + q4) * (16 / ELT));
-            lim[rt] = kAllVisible;
-        } else {
-#pragma unroll
-            for (int u = 0; u < KU4; ++u) qf[rt][u] = u32x4{0u, 0u, 0u, 0u};
-            lim[rt] = -1;
-        }
-    }
-
-    // Block ids of the item's key range go to LDS once: inside the ring
-    // they could only be vector loads, and waiting for those would also
-    // wait for the tile in flight. Q is waited for here for the same reason.
-    for (int i = tid; i < (ke - kb + PS_BLOCK - 1) / PS_BLOCK; i += 256) sbt[i] = bt[(kb >> 4) + i];
-    wait_vmcnt<0>();
-    __syncthreads();
 
     // 16-bit data: o carries one more tile, the row sums of P, formed on
     // MFMA against an all-ones V tile (rescaled with o, and summed over the
@@ -1032,6 +1006,54 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
             }
         }
     };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    // Tile 0's DMA goes out first, with its block ids read straight from the
+    // table (scalar loads), so that its latency overlaps the Q rows' and the
+    // staged ids' instead of following them.
+    const int ntiles = (ke - kb + TK - 1) / TK;
+    if (ntiles > 0) {
+        const int32_t *btk = bt + (kb >> 4);
+        IdVec id0;
+#pragma unroll
+        for (int b = 0; b < NSB; ++b) id0[b] = kb + 16 * b < ke ? btk[b] : 0;  // (unused past key_end)
+        issue_tile(S0{}, kb, id0);
+    }
+
+    u32x4 qf[RT][KU4];
+    int lim[RT];
+    ps_row grow[RT];   // gathered rows' map entries
+    if (!gathered) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            load_q_row<DT, D>(a, wr0 + rt * 16 + c, it.row_end, g, j, qs0, nc, q4, qf[rt], lim[rt]);
+    } else {
+        // (as in load_q_row: a row past the end reads the last row's map
+        // entry and query, unconditionally, and is never stored); all map
+        // entries first, then the queries they name
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int r = wr0 + rt * 16 + c;
+            grow[rt] = a.row_map[it.partial_row + (r < it.row_end ? r : it.row_end - 1)];
+            lim[rt] = r < it.row_end ? kAllVisible : -1;
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const T *qp = static_cast<const T *>(a.q) + (int64_t)grow[rt].q_row * D;
+#pragma unroll
+            for (int u = 0; u < KU4; ++u) qf[rt][u] = *reinterpret_cast<const u32x4 *>(qp + (u * 4 + q4) * (16 / ELT));
+        }
+    }
+
+    // Block ids of the item's key range go to LDS once: inside the ring
+    // they could only be vector loads, and waiting for those would also
+    // wait for the tile in flight. Q is waited for here for the same
+    // reason, and so is tile 0, issued together with them.
+    for (int i = tid; i < (ke - kb + PS_BLOCK - 1) / PS_BLOCK; i += 256) sbt[i] = bt[(kb >> 4) + i];
+    wait_vmcnt<0>();
+    __syncthreads();
 
     auto compute_tile = [&](auto stagec, int k0) {
         const uint8_t *ksm = stage(stagec);
@@ -1170,9 +1192,6 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
         __builtin_amdgcn_s_setprio(0);
     };
 
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
     // Tile ti sits in stage ti % NST; the NST - 1 tiles after it stream in
     // while it is consumed. One barrier per tile: once every thread's
     // loads of tile ti have landed, every wave has also finished tile
@@ -1202,9 +1221,7 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
         }
         if (active && k0 <= lim_hi) compute_tile(cur, k0);
     };
-    const int ntiles = (ke - kb + TK - 1) / TK;
     if (ntiles > 0) {
-        issue_tile(S0{}, kb, read_ids(kb));
         if constexpr (NST == 3) {
             const int k1 = ntiles > 1 ? kb + TK : kb;
             issue_tile(S1{}, k1, read_ids(k1));
