@@ -134,6 +134,45 @@ def test_layer_offset():
     check_out(st, out)
 
 
+def test_pool_offsets_past_4gib():
+    # The step's blocks moved into layer 1 of a two-layer pool whose layers
+    # are 4.3 GB each (K and V arrays of 8.6 GB): the layer starts past
+    # 4 GiB and the blocks sit near its top, so block addresses, DMA bases
+    # and scatter slots all need 64-bit offsets. The small pool's blocks
+    # (NaN where no sequence owns a slot) are copied to their new ids; the
+    # rest of the big pool is never written and must never be read.
+    st = workloads.random_step(23, dtype="bf16", num_q_heads=12, num_kv_heads=2, head_dim=128,
+                               num_seqs=6, max_q=70, max_ctx=700)
+    pk, pv = H.host_pools(st)
+    big_nb = 525_000   # x 8 KiB blocks = 4.3 GB per layer
+    new_id = big_nb - 1 - 7 * np.arange(st.num_blocks)   # distinct ids near the top
+    block_bytes = 16 * 2 * 128 * 2
+    # layer 1 starts past 4 GiB, and within it the ids straddle 4 GiB too
+    assert big_nb * block_bytes > 1 << 32 and new_id.min() * block_bytes < 1 << 32 < new_id.max() * block_bytes
+    _note(f"{st.summary()} big pool: 2 layers x {big_nb} blocks, ids {new_id.min()}..{new_id.max()}")
+    shape = (2, big_nb, 16, st.num_kv_heads, st.head_dim)
+    gk = torch.empty(shape, dtype=st.dtype, device=DEV)
+    gv = torch.empty(shape, dtype=st.dtype, device=DEV)
+    idx = torch.from_numpy(new_id).to(DEV)
+    gk[1, idx] = torch.from_numpy(pk[0]).to(DEV).view(st.dtype)
+    gv[1, idx] = torch.from_numpy(pv[0]).to(DEV).view(st.dtype)
+    tables = np.where(st.block_tables >= 0, new_id[np.maximum(st.block_tables, 0)], -1).astype(np.int32)
+    pool = P.make_pool(gk, gv, 1)
+    step = P.PackedStep(st.q_lens, st.num_computed, tables, st.num_q_heads, pool, DEV)
+    q, k, v = st.q.to(DEV), st.k.to(DEV), st.v.to(DEV)
+    out = torch.full_like(q, float("nan"))
+    step.run(q, k, v, pool, out, st.scale, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    check_out(st, out.cpu())
+    ek, ev = H.oracle_pools_after(st, pk, pv)
+    got_k = gk[1, idx].view(torch.int16).cpu().numpy()
+    got_v = gv[1, idx].view(torch.int16).cpu().numpy()
+    assert np.array_equal(got_k, ek[0]), "K blocks differ from the oracle's scatter"
+    assert np.array_equal(got_v, ev[0]), "V blocks differ from the oracle's scatter"
+    del gk, gv
+    torch.cuda.empty_cache()
+
+
 def test_single_key_rows_are_exact():
     # rows that see only key 0 (first token of a chunk at num_computed 0):
     # the weight is exactly 1, so the output is V[0] bit for bit
