@@ -68,7 +68,10 @@ typedef enum { PS_F32 = 0, PS_F16 = 1, PS_BF16 = 2 } ps_dtype;
  * contiguous (PageServe "06 Development history", phase 7: one pool
  * [layers, blocks, 16, H, D]; tinyserve README "How it works": K and V in
  * two slabs, H = number of KV heads). Every layer addresses the same block
- * ids; `layer` picks the layer a call works on.
+ * ids; `layer` picks the layer a call works on. Limits (else
+ * PS_ERR_UNSUPPORTED): num_blocks * 16 slots and the bytes of one block
+ * (16 * num_kv_heads * head_dim elements) each at most INT32_MAX; the
+ * arrays themselves may be any size (offsets are 64-bit).
  */
 typedef struct {
     void *k;

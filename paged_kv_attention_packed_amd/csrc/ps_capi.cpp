@@ -50,6 +50,8 @@ static ps_status check_cache_pool(const ps_pool *pool) {
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", pool->layer, pool->num_layers);
     if ((int64_t)pool->num_blocks * PS_BLOCK > INT32_MAX)
         return ps_fail(PS_ERR_UNSUPPORTED, "num_blocks %d: slots exceed int32", pool->num_blocks);
+    if (ps_block_bytes(pool) > INT32_MAX)
+        return ps_fail(PS_ERR_UNSUPPORTED, "num_kv_heads %d: a pool block exceeds INT32_MAX bytes", pool->num_kv_heads);
     return PS_OK;
 }
 
@@ -120,6 +122,9 @@ static ps_status check_pool_layout(const ps_pool *p, const char *what) {
         return ps_fail(PS_ERR_UNSUPPORTED, "%s pool: dtype %d", what, p->dtype);
     if (p->num_kv_heads < 1 || p->num_layers < 1 || p->num_blocks < 1)
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "%s pool needs num_kv_heads, num_layers, num_blocks >= 1", what);
+    if (ps_block_bytes(p) > INT32_MAX)
+        return ps_fail(PS_ERR_UNSUPPORTED, "%s pool: num_kv_heads %d: a block exceeds INT32_MAX bytes", what,
+                       p->num_kv_heads);
     return PS_OK;
 }
 

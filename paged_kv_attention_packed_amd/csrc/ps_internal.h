@@ -66,6 +66,14 @@ struct ps_merge {
 inline int ps_merge_rows(int head_dim) { return 1024 / head_dim; }
 static_assert(sizeof(ps_merge) == 32, "ps_merge layout");
 
+// Bytes of one pool block (16 slots of num_kv_heads x head_dim elements).
+// The kernels take a block's offset as a 32 x 32 -> 64-bit product of its
+// id and this size, so a pool whose block exceeds INT32_MAX bytes is
+// refused.
+inline int64_t ps_block_bytes(const ps_pool *p) {
+    return (int64_t)16 * p->num_kv_heads * p->head_dim * (p->dtype == PS_F32 ? 4 : 2);
+}
+
 // Tile geometry the planner and kernels agree on.
 constexpr int PS_BLOCK = 16;            // tokens per pool block
 constexpr int PS_DEC_TILE = 32;         // keys per decode-kernel wave iteration

@@ -944,6 +944,9 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
     const T *kp = static_cast<const T *>(a.pool_k) + a.layer_offset + (int64_t)j * D;
     const T *vp = static_cast<const T *>(a.pool_v) + a.layer_offset + (int64_t)j * D;
     const int kb = it.key_begin, ke = it.key_end;
+    // byte offset of pool block b (b < 2^31, 16 rows of at most 1 MiB)
+    const uint32_t bstride = (uint32_t)(PS_BLOCK * rs * ELT);
+    auto blk_bytes = [&](int64_t b) { return (uint64_t)(uint32_t)b * bstride; };
 
     const int wr0 = it.row_begin + wave * RPW;
     const bool active = wr0 < it.row_end;
@@ -998,11 +1001,14 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
             int64_t b = blk[r0 >> 4];
             if constexpr (RPI == 32) b = (trow >> 4) ? blk[(r0 >> 4) + 1] : b;
             const int inblk = (key & 15) * (int)rs + swz<ROWB>(tpos, key) * (16 / ELT);
+            // (block ids and the block stride fit 32 bits: one 32x32 -> 64
+            // multiply per block)
+            const char *bbase = reinterpret_cast<const char *>(kv ? vp : kp) + blk_bytes(b);
             if constexpr (RPI == 32) {  // one instruction spans two blocks: per-lane address
-                dma16((kv ? vp : kp) + b * 16 * rs + inblk, ring + i * 4096 + wave * 1024);
+                dma16(reinterpret_cast<const T *>(bbase) + inblk, ring + i * 4096 + wave * 1024);
             } else {  // scalar block base, loop-invariant lane offset, scalar LDS slot
                 const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring;
-                dma16_sv((kv ? vp : kp) + b * 16 * rs, (uint32_t)inblk * ELT, lds0 + i * 4096 + wave * 1024);
+                dma16_sv(bbase, (uint32_t)inblk * ELT, lds0 + i * 4096 + wave * 1024);
             }
         }
     };

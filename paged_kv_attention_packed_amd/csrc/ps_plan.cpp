@@ -97,6 +97,8 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", pool->layer, pool->num_layers);
     if ((int64_t)pool->num_blocks * PS_BLOCK > INT32_MAX)
         return ps_fail(PS_ERR_UNSUPPORTED, "num_blocks %d: slots exceed int32", pool->num_blocks);
+    if (ps_block_bytes(pool) > INT32_MAX)
+        return ps_fail(PS_ERR_UNSUPPORTED, "num_kv_heads %d: a pool block exceeds INT32_MAX bytes", pool->num_kv_heads);
     if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads != 0)
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
                        num_q_heads, pool->num_kv_heads);

@@ -133,6 +133,13 @@ def test_validation_errors():
         _expect_error(st, P.ps_plan_step, [1, 1], [3, 3], bt, 4, bad)
     # a valid plan with reads of a shared block is fine
     P.ps_plan_step([1, 1], [20, 20], np.array([[0, 1], [0, 3]]), 4, pool)
+    # limits: slots (num_blocks * 16) and a block's bytes must fit int32
+    big = P.ps_pool(0, 0, 1, (1 << 27), 16, 2, 64, P.PS_F16, 0)
+    _expect_error(UNS, P.ps_plan_step, [1, 1], [3, 3], bt, 4, big, match="slots")
+    wide = P.ps_pool(0, 0, 1, 8, 16, 1 << 18, 128, P.PS_F32, 0)
+    _expect_error(UNS, P.ps_plan_step, [1, 1], [3, 3], bt, 1 << 18, wide, match="block exceeds")
+    _expect_error(UNS, P.ps_reshape_and_cache, 1, 1, 1, 4, wide, match="block exceeds")
+    _expect_error(UNS, P.ps_copy_blocks, wide, wide, 1, 1, 1, match="block exceeds")
 
 
 def test_attention_argument_errors_return_before_any_launch():
