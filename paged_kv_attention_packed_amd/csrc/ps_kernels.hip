@@ -1346,16 +1346,42 @@ __global__ __launch_bounds__(256) void ps_merge_kernel(const ps_attn_launch a) {
     if (r >= mg.row_end) return;
     const int g = a.g;
     const int64_t p0 = (int64_t)mg.partial_row + row;
-    float M = kNegInf;
-    for (int sp = 0; sp < mg.num_splits; ++sp) M = fmaxf(M, a.ws_m[p0 + (int64_t)sp * mg.split_stride]);
-    const float muse = M == kNegInf ? 0.f : M;
-    float L = 0.f;
+    const int ns = mg.num_splits;
+    float M = kNegInf, L = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < mg.num_splits; ++sp) {
-        const int64_t pr = p0 + (int64_t)sp * mg.split_stride;
-        const float f = fast_exp2(a.ws_m[pr] - muse);
-        L += a.ws_l[pr] * f;
-        acc += *reinterpret_cast<const f32x4 *>(a.ws_acc + pr * D + d0) * f;
+    constexpr int MS = 8;
+    if (ns <= MS) {
+        // Every split's (m, l, acc) in one batch of loads, so the merge
+        // waits for memory once. Slots past the split count re-read split
+        // 0 (in bounds, finite) and take a zero weight: the sums are the
+        // same, term for term, as in the loop below.
+        float mv[MS], lv[MS];
+        f32x4 av[MS];
+#pragma unroll
+        for (int sp = 0; sp < MS; ++sp) {
+            const int64_t pr = p0 + (int64_t)(sp < ns ? sp : 0) * mg.split_stride;
+            mv[sp] = a.ws_m[pr];
+            lv[sp] = a.ws_l[pr];
+            av[sp] = *reinterpret_cast<const f32x4 *>(a.ws_acc + pr * D + d0);
+        }
+#pragma unroll
+        for (int sp = 0; sp < MS; ++sp) M = sp < ns ? fmaxf(M, mv[sp]) : M;
+        const float muse = M == kNegInf ? 0.f : M;
+#pragma unroll
+        for (int sp = 0; sp < MS; ++sp) {
+            const float f = sp < ns ? fast_exp2(mv[sp] - muse) : 0.f;
+            L += lv[sp] * f;
+            acc += av[sp] * f;
+        }
+    } else {
+        for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, a.ws_m[p0 + (int64_t)sp * mg.split_stride]);
+        const float muse = M == kNegInf ? 0.f : M;
+        for (int sp = 0; sp < ns; ++sp) {
+            const int64_t pr = p0 + (int64_t)sp * mg.split_stride;
+            const float f = fast_exp2(a.ws_m[pr] - muse);
+            L += a.ws_l[pr] * f;
+            acc += *reinterpret_cast<const f32x4 *>(a.ws_acc + pr * D + d0) * f;
+        }
     }
     const int tok = div_g(a, r);
     const int h = mg.kv_head * g + (r - tok * g);
