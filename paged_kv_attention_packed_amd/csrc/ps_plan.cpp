@@ -399,6 +399,18 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
             delete p;
             return ps_fail(PS_ERR_UNSUPPORTED, "split-K workspace too large");
         }
+        // Longest decode items first (longest-processing-time order): in a
+        // launch with more items than resident workgroups the ones that
+        // start late are the short ones, and in a mixed launch the longest
+        // decode items start next to prefill items. Measured on MI355X: C4
+        // -10%, C3 -5%; a decode-only launch whose items all start at once
+        // (C2, 128 items) gains nothing and keeps the sequence order.
+        // Nothing else depends on the order: merges and partials are
+        // addressed by workspace row.
+        if (!pre.empty() || dec.size() > 256)
+            std::stable_sort(dec.begin(), dec.end(), [](const ps_item &x, const ps_item &y) {
+                return x.key_end - x.key_begin > y.key_end - y.key_begin;
+            });
         p->dec_rt = dec_rt;
         p->ws_rows = ws_rows;
         p->n_dec = (int32_t)dec.size();
