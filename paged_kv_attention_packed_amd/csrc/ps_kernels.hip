@@ -1316,8 +1316,13 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
 // Decode and prefill items of one step in a single launch, so that the
 // memory-bound decode items and the MFMA-bound prefill items share the
 // CUs instead of running one kernel after the other. Block b < 2 min(nd,
-// np) alternates decode / prefill items (each CU starts with one of each),
-// the remaining blocks take what is left. Decode items run 4 waves.
+// np) alternates decode / prefill items, the remaining blocks take what is
+// left. Decode items run 4 waves. Workgroups go to the 8 XCDs round-robin
+// by block index, so in the alternating part the decode items run on the
+// even XCDs and the prefill items on the odd ones: the prefill items,
+// which read the same keys (one chunk's context, or a shared prefix),
+// then share four L2s. Mappings that give every XCD both kinds (runs of 8
+// or 256 blocks) measured 0-3% slower.
 template <class DT, int D, int RT>
 __global__ __launch_bounds__(256, 2) void ps_mixed_kernel(const ps_attn_launch a) {
     __shared__ union {
