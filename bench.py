@@ -488,6 +488,38 @@ def main():
     torch.cuda.synchronize()
     ms_call = e0.elapsed_time(e1) / args.steps
 
+    # ---- the prefill chunks alone: their sequences planned on their own
+    # (the step's other sequences left out), the attention call timed over
+    # the same pool copies; FLOPs over that time give the prefill kernel's
+    # share of the MFMA peak
+    prefill_alone = None
+    g = step.num_q_heads // step.num_kv_heads
+    pre = [s for s in range(len(step.q_lens)) if g * int(step.q_lens[s]) > 32]   # the planner's rule
+    if pre:
+        qsl = np.concatenate([[0], np.cumsum(step.q_lens)])
+        rows = torch.cat([torch.arange(int(qsl[s]), int(qsl[s + 1])) for s in pre]).to(dev)
+        q_pre = q.index_select(0, rows).contiguous()
+        out_pre = torch.empty_like(q_pre)
+        ps_pre = P.PackedStep(step.q_lens[pre], step.num_computed[pre], step.block_tables[pre],
+                              step.num_q_heads, pool0, dev, stream=stream)
+        for i in range(args.warmup):
+            ps_pre.attention(q_pre, pools[i % nrot], out_pre, step.scale, stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            ps_pre.attention(q_pre, pools[i % nrot], out_pre, step.scale, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_pre = e0.elapsed_time(e1) / args.steps
+        pflops = ps_pre.info["flops_prefill"]
+        peak_pre = MFMA_PEAK_TFLOPS if step.dtype_name != "f32" else FP32_PEAK_TFLOPS
+        tf_pre = pflops / (ms_pre * 1e-3) / 1e12
+        prefill_alone = {"call": "ps_paged_attention over the prefill sequences alone (prefill kernel + merge)",
+                         "sequences": len(pre), "prefill_items": ps_pre.info["prefill_items"],
+                         "merge_items": ps_pre.info["merge_items"], "us": round(ms_pre * 1e3, 3),
+                         "gflop": round(pflops / 1e9, 3), "bound": "mfma", "achieved": round(tf_pre, 1),
+                         "peak": peak_pre, "unit": "TFLOP/s", "frac": round(tf_pre / peak_pre, 4)}
+
     T = step.num_tokens
     tok_s = T / (ms_step * 1e-3)
     # algorithmic bytes of one attention call: each visible K/V row once per
@@ -571,6 +603,7 @@ def main():
         "kv_read_gbs": round(kv_bytes / (ms_attn * 1e-3) / 1e9, 1),
         "attention_tflops": round(flops / (ms_attn * 1e-3) / 1e12, 2),
         "scatter_us": round(ms_scatter * 1e3, 3),
+        "prefill_alone": prefill_alone,
         "host_plan_us": round(host_plan_us, 1),
         "pool_copies": nrot,
         "launch": "eager" if args.eager else "hip-graph replay",
