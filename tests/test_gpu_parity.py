@@ -125,6 +125,33 @@ def test_random_ragged_steps(case, flags):
         check_out(st, out)
 
 
+SPREAD_CASES = [  # dtype, Hq, Hkv, D, q_lens, num_computed
+    ("f16", 12, 2, 128, [1, 1, 1, 300], [39, 199, 512, 700]),
+    ("bf16", 14, 2, 64, [1, 1, 1, 1, 1, 250], [16, 59, 299, 999, 32, 400]),
+]
+
+
+@pytest.mark.parametrize("case", SPREAD_CASES, ids=["f16-128", "bf16-64"])
+def test_mixed_launch_with_many_prefill_items(case):
+    # With at least twice as many prefill-kernel items as decode items the
+    # mixed launch spreads the decode items over whole rounds of 8 blocks;
+    # counts that are not multiples of 8 leave a remainder that closes the
+    # launch. Both are checked against the oracle here.
+    dt, hq, hkv, d, q_lens, nc = case
+    st = workloads.build_step(f"mixed-spread-{dt}-{d}", 11, dt, hq, hkv, d, 256, q_lens, nc)
+    proto = P.ps_pool(0, 0, st.num_layers, st.num_blocks, 16, st.num_kv_heads, st.head_dim,
+                      P._binding.dtype_code(st.dtype), st.layer)
+    info = P.ps_plan_get_info(P.ps_plan_step(st.q_lens, st.num_computed, st.block_tables,
+                                             st.num_q_heads, proto))
+    nd, npf = info["decode_items"], info["prefill_items"]
+    _note(f"{st.name}: {nd} decode items, {npf} prefill items, {info['merge_items']} merges")
+    assert nd > 0 and npf >= 2 * nd and (nd % 8 or npf % 8)
+    pools = H.host_pools(st)
+    out, gk, gv = run_on_gpu(st, pools=pools)
+    check_pool(st, pools, gk, gv)
+    check_out(st, out)
+
+
 def test_layer_offset():
     st = workloads.random_step(5, dtype="bf16", num_q_heads=12, num_kv_heads=2, head_dim=128,
                                num_seqs=5, max_q=40, max_ctx=200, num_layers=3, layer=1)
