@@ -9,9 +9,13 @@ split-K merge). The host planner's metadata is built and uploaded once
 before timing (inputs resident in HBM); its host cost is reported as
 ``host_plan_us``.
 
-Default workload: the Qwen2.5-0.5B-shaped decode step (64 sequences,
-context U[16, 512], 14 Q / 2 KV heads, D 64, fp16). ``--config N`` picks
-another of the five named steps.
+Default workload: the long-context speculative-verify step (32 sequences
+at context 32768 with 5 causal query tokens each, plus one 2048-token
+prefill chunk at position 30000; 12 Q / 2 KV heads, D 128, bf16), the
+largest of the five named steps and the one that carries both the HBM
+target (verify rows) and the MFMA target (the chunk). ``--config N``
+picks another. Sub-lines time the prefill chunks alone (MFMA fraction)
+and the decode / verify rows alone (HBM fraction) over the same pools.
 
 The pool is replicated so that consecutive timed steps touch different
 copies and the working set exceeds the 256 MB Infinity Cache plus L2:
@@ -53,7 +57,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="plan with PS_PLAN_SHARED_PREFIX (attention over blocks shared by several "
+                         "tables runs once; output bits then depend on the sharing)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
@@ -63,11 +70,13 @@ def parse():
                     help="time steps as individual launches instead of replaying them from a "
                          "captured HIP graph")
     ap.add_argument("--op", default="step",
-                    choices=["step", "copy-blocks", "swap-blocks", "rope-cache", "spec-verify"],
+                    choices=["step", "copy-blocks", "swap-blocks", "rope-cache", "spec-verify", "fixed-graph"],
                     help="step: the packed step (default); copy-blocks: copy-on-write block copies "
                          "in one device pool; swap-blocks: blocks out to a pinned host pool and back; "
                          "rope-cache: rotary embedding of the step's q and k fused with the KV scatter; "
-                         "spec-verify: rejection sampling over the step's verify rows (use --config 5)")
+                         "spec-verify: rejection sampling over the step's verify rows (use --config 5); "
+                         "fixed-graph: one captured graph of a fixed-shape decode plan replayed over "
+                         "steps of different lengths, against eager launches (use --config 2)")
     ap.add_argument("--proposer", default="draft", choices=["draft", "ngram"],
                     help="spec-verify: draft-model or n-gram proposer distributions")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -120,8 +129,25 @@ def fill_context(P, step, pool, dev, stream):
         del ps, kk, vv
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(step, seconds):
-    """The fp64 oracle (scatter + attention of the whole step) on host cores."""
+    """The fp64 oracle (scatter + attention of the whole step) on host cores.
+
+    A step whose attention takes the oracle longer than ``seconds`` is
+    sampled: the scatter runs whole, attention runs on a uniform random
+    sample of (token, head) rows sized to take about ``seconds``, and the
+    rate is that of the whole step extrapolated from the sample's time per
+    row."""
     import numpy as np
     import torch
     import oracle
@@ -141,18 +167,44 @@ def cpu_baseline(step, seconds):
         c0 += c
     q, kc, vc, k, v = (t.to(torch.float64).numpy() for t in (step.q, step.k_ctx, step.v_ctx, step.k, step.v))
     kb, vb = bits(step.k), bits(step.v)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.reshape_and_cache(pk, pv, step.layer, kb, vb, step.q_lens, step.num_computed,
-                                 step.block_tables)
-        oracle.attention(q, kc, vc, k, v, step.q_lens, step.num_computed, step.scale)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 10000:
-            break
-    return {"value": round(reps * step.num_tokens / el, 3), "unit": "query tok/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{reps} full steps of {step.name} (scatter + attention, fp64) in {el:.1f} s"}
+    T, H = step.num_tokens, step.num_q_heads
+    rows = T * H
+    rng = np.random.default_rng(12345)
+
+    def attend(n_rows):
+        sel = None
+        if n_rows < rows:
+            sel = np.zeros(rows, dtype=bool)
+            sel[rng.choice(rows, size=n_rows, replace=False)] = True
+            sel = sel.reshape(T, H)
+        t0 = time.perf_counter()
+        oracle.attention(q, kc, vc, k, v, step.q_lens, step.num_computed, step.scale, row_sel=sel)
+        return time.perf_counter() - t0
+
+    t0 = time.perf_counter()
+    oracle.reshape_and_cache(pk, pv, step.layer, kb, vb, step.q_lens, step.num_computed, step.block_tables)
+    t_scatter = time.perf_counter() - t0
+    # calibrate on a small sample, then size the timed one
+    n0 = max(1, min(rows, 4 * oracle.num_threads()))
+    per_row = attend(n0) / n0
+    n = int(min(rows, max(n0, seconds / max(per_row, 1e-9))))
+    if n >= rows:
+        reps, t_attn = 0, 0.0
+        while True:
+            t_attn += attend(rows)
+            reps += 1
+            if t_attn >= seconds or reps >= 10000:
+                break
+        t_step = t_scatter + t_attn / reps
+        sample = f"{reps} full steps of {step.name} (scatter + attention, fp64) in {t_attn:.1f} s"
+    else:
+        t_attn = attend(n)
+        t_step = t_scatter + t_attn * rows / n
+        sample = (f"{step.name}: scatter of all {T} tokens ({t_scatter * 1e3:.1f} ms) + attention on a "
+                  f"uniform sample of {n} of {rows} (token, head) rows in {t_attn:.1f} s, scaled to the "
+                  f"whole step ({t_step:.1f} s)")
+    return {"value": round(T / t_step, 3), "unit": "query tok/s",
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu": cpu_model(), "sample": sample}
 
 
 def bench_blocks(args):
@@ -351,6 +403,123 @@ def bench_spec(args):
     print(json.dumps(result), flush=True)
 
 
+def time_calls(fn, n, warmup, stream):
+    """Average seconds per call of fn(i) over n calls on ``stream`` (HIP
+    events recorded on the stream the kernels are launched on)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e-3
+
+
+def sub_step(P, step, seqs, flags, pool0, dev, stream, q):
+    """The step's sequences `seqs` planned on their own: (PackedStep, q rows, out)."""
+    import numpy as np
+    import torch
+    qsl = np.concatenate([[0], np.cumsum(step.q_lens)])
+    rows = torch.cat([torch.arange(int(qsl[s]), int(qsl[s + 1])) for s in seqs]).to(dev)
+    q_sub = q.index_select(0, rows).contiguous()
+    ps = P.PackedStep(step.q_lens[seqs], step.num_computed[seqs], step.block_tables[seqs],
+                      step.num_q_heads, pool0, dev, flags, stream=stream)
+    return ps, q_sub, torch.empty_like(q_sub)
+
+
+def bench_fixed_graph(args):
+    """NEXT-1 across steps: a fixed-shape decode plan (PS_PLAN_FIXED_SHAPE)
+    captured once into a HIP graph and replayed over steps of different
+    lengths (each step's plan uploaded into the same metadata buffer first,
+    outside the timed replay), against the same steps launched eagerly."""
+    import numpy as np
+    import torch
+    import paged_kv_attention_packed_amd as P
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    base = workloads.config(args.config, values=False)
+    hq, hkv, d, dt = base.num_q_heads, base.num_kv_heads, base.head_dim, base.dtype
+    S_max = base.num_seqs
+    max_ctx = int((base.num_computed + base.q_lens).max())
+    width = -(-max_ctx // 16)
+    n_steps = 8
+    steps = []
+    for i in range(n_steps):   # same distribution as the named step, new lengths each step
+        rng = np.random.default_rng(4000 + i)
+        ctx = rng.integers(16, max_ctx, size=S_max, endpoint=True)
+        steps.append(workloads.build_step(f"{base.name}-step{i}", 4000 + i, base.dtype_name, hq, hkv, d,
+                                          base.num_blocks, [1] * S_max, (ctx - 1).tolist(), rng=rng,
+                                          table_width=width, values=False))
+    opts = P.plan_options(max_seqs=S_max, max_tokens=S_max, max_query_len=1)
+    proto = P.ps_pool(0, 0, 1, base.num_blocks, 16, hkv, d, P._binding.dtype_code(dt), 0)
+    shape = (1, base.num_blocks, 16, hkv, d)
+    pk = torch.randn(shape, device=dev).to(dt)
+    pv = torch.randn(shape, device=dev).to(dt)
+    pool = P.make_pool(pk, pv)
+    fixed = [P.ps_plan_step(st.q_lens, st.num_computed, st.block_tables, hq, proto, P.PS_PLAN_FIXED_SHAPE, opts)
+             for st in steps]
+    meta_bytes, ws_bytes = P.ps_plan_sizes(fixed[0])
+    meta = torch.empty(meta_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    q = torch.randn((S_max, hq, d), device=dev).to(dt)
+    k = torch.randn((S_max, hkv, d), device=dev).to(dt)
+    v = torch.randn((S_max, hkv, d), device=dev).to(dt)
+    out = torch.empty_like(q)
+
+    def call(plan, st, cs):
+        a = P.ps_plan_device_arrays(plan)
+        P.ps_step(q, k, v, a.slot_mapping, pool, a.block_tables, a.block_table_stride, a.query_start_loc,
+                  a.num_computed_tokens, a.context_lens, out, st.num_seqs, st.num_tokens, hq, base.scale,
+                  plan, ws, ws_bytes, cs)
+
+    P.ps_plan_upload(fixed[0], meta, meta_bytes, stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(fixed[0], steps[0], torch.cuda.current_stream())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, args.steps // n_steps)
+    t_graph = t_eager = 0.0
+    for i, st in enumerate(steps):
+        P.ps_plan_upload(fixed[i], meta, meta_bytes, stream)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_graph += e0.elapsed_time(e1) / reps
+        for _ in range(3):
+            call(fixed[i], st, stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            call(fixed[i], st, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_eager += e0.elapsed_time(e1) / reps
+    t_graph /= n_steps
+    t_eager /= n_steps
+    plan_us = float(np.mean([P.ps_plan_get_info(p)["plan_us"] for p in fixed]))
+    result = {"metric": "fixed-shape decode step: HIP-graph replay vs eager launch, 1 MI355X",
+              "value": round(t_graph * 1e3, 3), "unit": "us per step (graph replay)", "higher_is_better": False,
+              "eager_us": round(t_eager * 1e3, 3), "graph_vs_eager": round(t_graph / t_eager, 4),
+              "host_plan_us": round(plan_us, 1),
+              "n_gpus": 1, "steps": reps * n_steps, "warmup": 3, "dtype": base.dtype_name, "data": "synthetic",
+              "config": {"workload": f"{base.name}: {n_steps} steps of {S_max} decodes, context U[16, {max_ctx}]",
+                         "op": args.op, "max_seqs": S_max, "decode_items": P.ps_plan_get_info(fixed[0])["decode_items"]}}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -363,6 +532,9 @@ def main():
     if args.op == "spec-verify":
         bench_spec(args)
         return
+    if args.op == "fixed-graph":
+        bench_fixed_graph(args)
+        return
     if args.op != "step":
         bench_blocks(args)
         return
@@ -374,16 +546,20 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     step = workloads.config(args.config)
-    log(f"workload {step.summary()}")
+    flags = P.PS_PLAN_SHARED_PREFIX if args.shared_prefix else P.PS_PLAN_DEFAULT
+    log(f"workload {step.summary()} flags {flags}")
 
-    # ---- plan (host), timed separately
+    # ---- plan (host): the planner's own clock, and the Python call
     proto = P.ps_pool(0, 0, step.num_layers, step.num_blocks, 16, step.num_kv_heads,
                       step.head_dim, P._binding.dtype_code(step.dtype), step.layer)
-    t0 = time.perf_counter()
     nplan = 20
+    plan_us = []
+    t0 = time.perf_counter()
     for _ in range(nplan):
-        P.ps_plan_step(step.q_lens, step.num_computed, step.block_tables, step.num_q_heads, proto)
-    host_plan_us = (time.perf_counter() - t0) / nplan * 1e6
+        pl = P.ps_plan_step(step.q_lens, step.num_computed, step.block_tables, step.num_q_heads, proto, flags)
+        plan_us.append(P.ps_plan_get_info(pl)["plan_us"])
+        del pl
+    host_call_us = (time.perf_counter() - t0) / nplan * 1e6
 
     # ---- pools: one filled copy, replicated
     shape = (step.num_layers, step.num_blocks, 16, step.num_kv_heads, step.head_dim)
@@ -393,8 +569,9 @@ def main():
     fill_context(P, step, pool0, dev, stream)
 
     ps = P.PackedStep(step.q_lens, step.num_computed, step.block_tables, step.num_q_heads, pool0,
-                      dev, stream=stream)
+                      dev, flags, stream=stream)
     info = ps.info
+    kinds = P.ps_plan_sequence_kernels(ps.plan, step.num_seqs)
     kv_bytes = info["kv_bytes_decode"] + info["kv_bytes_prefill"]
     touched = info["kv_bytes_unique"] + info["q_bytes"] + info["out_bytes"] + info["scatter_bytes"]
     pool_bytes = 2 * pk0.numel() * pk0.element_size()
@@ -458,67 +635,48 @@ def main():
         torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # ---- attention call alone (the dominant kernel(s)), same rotation
-    for i in range(args.warmup):
-        ps.attention(q, pools[i % nrot], outs[0], step.scale, stream)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        ps.attention(q, pools[i % nrot], outs[i % len(outs)], step.scale, stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_attn = e0.elapsed_time(e1) / args.steps
-
-    # ---- scatter alone
-    e0.record(stream)
-    for i in range(args.steps):
-        ps.reshape_and_cache(k, v, pools[i % nrot], stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_scatter = e0.elapsed_time(e1) / args.steps
-
-    # ---- the step call alone, eager: when the planner fuses the scatter
-    # into the attention launch (every non-prefix item on the decode
-    # kernel), ps_step is that one launch (plus the split-K merge)
+    # ---- the calls alone, eager, same rotation
+    ms_attn = 1e3 * time_calls(lambda i: ps.attention(q, pools[i % nrot], outs[i % len(outs)], step.scale, stream),
+                               args.steps, args.warmup, stream)
+    ms_scatter = 1e3 * time_calls(lambda i: ps.reshape_and_cache(k, v, pools[i % nrot], stream),
+                                  args.steps, 0, stream)
+    # when the planner fuses the scatter into the attention launch (every
+    # non-prefix item on the decode kernel), ps_step is that one launch
+    # (plus the split-K merge)
     fused = info["step_fused"] == 1
-    e0.record(stream)
-    for i in range(args.steps):
-        ps.step(q, k, v, pools[i % nrot], outs[i % len(outs)], step.scale, stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_call = e0.elapsed_time(e1) / args.steps
+    ms_call = 1e3 * time_calls(lambda i: ps.step(q, k, v, pools[i % nrot], outs[i % len(outs)], step.scale, stream),
+                               args.steps, 0, stream)
 
-    # ---- the prefill chunks alone: their sequences planned on their own
-    # (the step's other sequences left out), the attention call timed over
-    # the same pool copies; FLOPs over that time give the prefill kernel's
-    # share of the MFMA peak
-    prefill_alone = None
-    g = step.num_q_heads // step.num_kv_heads
-    pre = [s for s in range(len(step.q_lens)) if g * int(step.q_lens[s]) > 32]   # the planner's rule
-    if pre:
-        qsl = np.concatenate([[0], np.cumsum(step.q_lens)])
-        rows = torch.cat([torch.arange(int(qsl[s]), int(qsl[s + 1])) for s in pre]).to(dev)
-        q_pre = q.index_select(0, rows).contiguous()
-        out_pre = torch.empty_like(q_pre)
-        ps_pre = P.PackedStep(step.q_lens[pre], step.num_computed[pre], step.block_tables[pre],
-                              step.num_q_heads, pool0, dev, stream=stream)
-        for i in range(args.warmup):
-            ps_pre.attention(q_pre, pools[i % nrot], out_pre, step.scale, stream)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(args.steps):
-            ps_pre.attention(q_pre, pools[i % nrot], out_pre, step.scale, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_pre = e0.elapsed_time(e1) / args.steps
+    # ---- each kind of sequence alone, planned on its own (the step's other
+    # sequences left out), its attention call timed over the same pools:
+    # the prefill chunks against the MFMA peak, the decode / verify rows
+    # against HBM
+    peak_mfma = MFMA_PEAK_TFLOPS if step.dtype_name != "f32" else FP32_PEAK_TFLOPS
+    prefill_alone = decode_alone = None
+    pre = [s for s in range(step.num_seqs) if kinds[s] == 1]
+    dec = [s for s in range(step.num_seqs) if kinds[s] != 1]
+    if pre and dec:
+        ps_pre, q_pre, out_pre = sub_step(P, step, pre, flags, pool0, dev, stream, q)
+        ms_pre = 1e3 * time_calls(lambda i: ps_pre.attention(q_pre, pools[i % nrot], out_pre, step.scale, stream),
+                                  args.steps, args.warmup, stream)
         pflops = ps_pre.info["flops_prefill"]
-        peak_pre = MFMA_PEAK_TFLOPS if step.dtype_name != "f32" else FP32_PEAK_TFLOPS
         tf_pre = pflops / (ms_pre * 1e-3) / 1e12
         prefill_alone = {"call": "ps_paged_attention over the prefill sequences alone (prefill kernel + merge)",
                          "sequences": len(pre), "prefill_items": ps_pre.info["prefill_items"],
                          "merge_items": ps_pre.info["merge_items"], "us": round(ms_pre * 1e3, 3),
                          "gflop": round(pflops / 1e9, 3), "bound": "mfma", "achieved": round(tf_pre, 1),
-                         "peak": peak_pre, "unit": "TFLOP/s", "frac": round(tf_pre / peak_pre, 4)}
+                         "peak": peak_mfma, "unit": "TFLOP/s", "frac": round(tf_pre / peak_mfma, 4)}
+        ps_dec, q_dec, out_dec = sub_step(P, step, dec, flags, pool0, dev, stream, q)
+        ms_dec = 1e3 * time_calls(lambda i: ps_dec.attention(q_dec, pools[i % nrot], out_dec, step.scale, stream),
+                                  args.steps, args.warmup, stream)
+        di = ps_dec.info
+        dbytes = di["kv_bytes_unique"] + di["q_bytes"] + di["out_bytes"] + di["table_bytes"]
+        gbs_dec = dbytes / (ms_dec * 1e-3) / 1e9
+        decode_alone = {"call": "ps_paged_attention over the decode / verify sequences alone (decode kernel + merge)",
+                        "sequences": len(dec), "decode_items": di["decode_items"], "merge_items": di["merge_items"],
+                        "us": round(ms_dec * 1e3, 3), "algorithmic_bytes": dbytes,
+                        "kv_bytes_unique": di["kv_bytes_unique"], "bound": "hbm", "achieved": round(gbs_dec, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_dec / HBM_PEAK_GBS, 4)}
 
     T = step.num_tokens
     tok_s = T / (ms_step * 1e-3)
@@ -537,22 +695,16 @@ def main():
     if os.path.exists(args.traffic):
         try:
             with open(args.traffic) as f:
-                tr = json.load(f).get(step.name)
+                tr = json.load(f).get(step.name + ("+shared-prefix" if args.shared_prefix else ""))
             if tr and tr.get("kernel_source_digest") == kernel_source_digest():
                 traffic = tr["bytes_per_launch"]
         except (OSError, ValueError, KeyError):
             traffic = None
     flops = info["flops_decode"] + info["flops_prefill"]
     nd, npf = info["decode_items"], info["prefill_items"]
-    # 16-bit steps with both kinds of item run them in one launch (the
-    # library's default kernel shape; PS_MIXED=0 or another prefill variant
-    # launches them one after the other)
-    mixed = (nd > 0 and npf > 0 and step.dtype_name != "f32"
-             and os.environ.get("PS_MIXED", "1") != "0"
-             and os.environ.get("PS_PREFILL_VARIANT", "0") == "0")
     npx = info["prefix_items"]
     pre_note = f"{npf} prefill items, {npx} of them shared-prefix" if npx else f"{npf} prefill items"
-    if mixed:
+    if info["mixed_launch"]:
         kernels = [f"ps_mixed_kernel x{nd + npf} ({nd} decode + {pre_note})"]
     else:
         kernels = ([f"ps_decode_kernel x{nd}"] if nd else []) + \
@@ -562,15 +714,13 @@ def main():
     # the launch's bound is the larger of its two ideal times: algorithmic
     # bytes at HBM peak, or its QK^T and PV flops at dense 16-bit MFMA peak
     # (fp32 rows run v_mfma_f32_16x16x4f32, priced at the fp32 matrix peak)
-    mfma_peak = MFMA_PEAK_TFLOPS if step.dtype_name != "f32" else FP32_PEAK_TFLOPS
     t_hbm = dom_bytes / (HBM_PEAK_GBS * 1e9)
-    dom_flops = flops
-    t_mfma = dom_flops / (mfma_peak * 1e12)
+    t_mfma = flops / (peak_mfma * 1e12)
     hbm_line = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    tflops_dom = dom_flops / (ms_dom * 1e-3) / 1e12
-    mfma_line = {"bound": "mfma", "achieved": round(tflops_dom, 1), "peak": mfma_peak,
-                 "unit": "TFLOP/s", "frac": round(tflops_dom / mfma_peak, 4)}
+    tflops_dom = flops / (ms_dom * 1e-3) / 1e12
+    mfma_line = {"bound": "mfma", "achieved": round(tflops_dom, 1), "peak": peak_mfma,
+                 "unit": "TFLOP/s", "frac": round(tflops_dom / peak_mfma, 4)}
     if t_mfma > t_hbm:
         roofline, other = dict(mfma_line), hbm_line
     else:
@@ -590,21 +740,31 @@ def main():
         "vs_baseline": None,
         "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16"}[step.dtype_name],
         "data": "synthetic",
-        "config": {"workload": step.name, "num_seqs": step.num_seqs, "num_tokens": T,
+        "config": {"workload": step.name + (" +shared-prefix pass" if args.shared_prefix else ""),
+                   "num_seqs": step.num_seqs, "num_tokens": T,
                    "num_q_heads": step.num_q_heads, "num_kv_heads": step.num_kv_heads,
                    "head_dim": step.head_dim, "block_size": 16, "num_blocks": step.num_blocks,
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "roofline_other_bound": other,
         "dominant": {"call": dom_call, "kernels": kernels,
-                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "algorithmic_bytes_per_launch": dom_bytes, "flops_per_launch": flops,
                      "us_per_launch": round(ms_dom * 1e3, 3)},
+        "prefill_alone": prefill_alone,
+        "decode_alone": decode_alone,
         "attention_alone_us": round(ms_attn * 1e3, 3),
-        "kv_read_gbs": round(kv_bytes / (ms_attn * 1e-3) / 1e9, 1),
+        # KV bytes over the attention call's time: unique (each physical
+        # block once: what HBM can serve) and logical (once per sequence
+        # that reads it; above HBM speed when blocks are shared and cached)
+        "kv_read_gbs": round(info["kv_bytes_unique"] / (ms_attn * 1e-3) / 1e9, 1),
+        "kv_read_logical_gbs": round(kv_bytes / (ms_attn * 1e-3) / 1e9, 1),
         "attention_tflops": round(flops / (ms_attn * 1e-3) / 1e12, 2),
         "scatter_us": round(ms_scatter * 1e3, 3),
-        "prefill_alone": prefill_alone,
-        "host_plan_us": round(host_plan_us, 1),
+        "host_plan_us": round(min(plan_us), 1),
+        "host_plan_call_us": round(host_call_us, 1),
+        "plan": {key: info[key] for key in ("decode_items", "prefill_items", "merge_items", "decode_split_keys",
+                                            "prefill_split_keys", "decode_waves", "mixed_launch", "step_fused",
+                                            "workspace_rows", "flags")},
         "pool_copies": nrot,
         "launch": "eager" if args.eager else "hip-graph replay",
         "gpu": torch.cuda.get_device_name(0),
@@ -627,7 +787,6 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline ...")
         result["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds)
-        result["cpu_baseline"]["cpu"] = platform.processor() or platform.machine()
     print(json.dumps(result), flush=True)
 
 

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PS_ABI_VERSION 3
+#define PS_ABI_VERSION 4
 
 typedef int32_t ps_status;
 enum {
@@ -92,12 +92,66 @@ typedef struct {
  */
 typedef struct ps_plan ps_plan;
 
-/* ps_plan_step flags: which attention kernel serves each sequence. */
+/*
+ * ps_plan_step flags. The low two bits choose the attention kernel of each
+ * sequence; the others are independent switches.
+ */
 enum {
-    PS_PLAN_DEFAULT = 0,      /* few query rows per KV head: split-K decode kernel; else prefill kernel */
-    PS_PLAN_ALL_DECODE = 1,   /* every sequence through the decode/verify kernel */
-    PS_PLAN_ALL_PREFILL = 2   /* every sequence through the prefill-chunk kernel */
+    PS_PLAN_DEFAULT = 0,        /* few query rows per KV head (g * n_s <= 32): split-K decode kernel; else prefill kernel */
+    PS_PLAN_ALL_DECODE = 1,     /* every sequence through the decode/verify kernel (g * n_s <= 32 required per work item row range) */
+    PS_PLAN_ALL_PREFILL = 2,    /* every sequence through the prefill-chunk kernel */
+    /* Shared-prefix pass (opt-in). Decode sequences whose tables open with
+     * the same physical blocks (blocks shared by reference: PageServe "03
+     * Paged KV cache"; tinyserve README "How it works", copy-on-write)
+     * form groups; attention over a group's common blocks then runs once,
+     * on rows gathered from every member, and merges with each member's
+     * own keys like a key split. The result is the same softmax summed in
+     * another order, so with this flag the output bits depend on which
+     * blocks are physically shared. Without it (the default) a step gives
+     * the same bits whether its prefix blocks are shared or private
+     * copies. Applies with PS_PLAN_DEFAULT routing only. */
+    PS_PLAN_SHARED_PREFIX = 4,
+    /* Decode and prefill items in two launches (decode kernel, then
+     * prefill kernel) instead of one launch that runs both kinds. Same
+     * results bit for bit; a measurement switch. */
+    PS_PLAN_SEPARATE_LAUNCHES = 8,
+    /* Graph-replayable shape: the metadata layout, the launch grids and
+     * every kernel argument depend only on the options' capacities (and
+     * the geometry), not on this step's lengths. Steps planned with the
+     * same options, uploaded into the same metadata buffer, can replay one
+     * captured graph of ps_step / ps_paged_attention. Work lists are
+     * padded with idle items that exit at once. Every sequence must take
+     * the decode kernel (no PS_PLAN_ALL_PREFILL, no shared-prefix pass). */
+    PS_PLAN_FIXED_SHAPE = 16
 };
+
+/*
+ * Tuning and capacity options of ps_plan_step (NULL = all zero = chosen by
+ * the planner). Every choice is recorded in ps_plan_info; nothing outside
+ * the arguments (no environment variable) changes a plan.
+ */
+typedef struct {
+    int32_t decode_split_keys;   /* keys per decode work item: 0 = planner's choice, else a
+                                    multiple of 16 in [16, 16384] */
+    int32_t prefill_split_keys;  /* keys per prefill work item: 0 = planner's choice, else a
+                                    multiple of 64 in [64, 16384] */
+    int32_t decode_waves;        /* waves per decode workgroup: 0 = planner's choice, 4 or 8
+                                    (16 for head_dim 64 16-bit steps of one row tile) */
+    int32_t prefix_min_seqs;     /* PS_PLAN_SHARED_PREFIX: members a group needs (0 = 8; >= 2) */
+    int32_t prefix_min_keys;     /* ... tokens each member shares with the group's first
+                                    (0 = 256; >= 16) */
+    int32_t prefix_slice_keys;   /* ... keys per prefix work item: 0 = planner's choice, else a
+                                    multiple of 64 in [64, 16384] */
+    /* PS_PLAN_FIXED_SHAPE capacities (ignored otherwise): */
+    int32_t max_seqs;            /* >= num_seqs */
+    int32_t max_tokens;          /* >= num_tokens */
+    int32_t max_query_len;       /* >= every q_lens[s]; (num_q_heads / num_kv_heads) *
+                                    max_query_len <= 32 */
+    int32_t max_decode_items;    /* 0 = max_seqs * num_kv_heads */
+    int32_t max_merge_items;     /* 0: no key splits allowed */
+    int32_t max_workspace_rows;  /* split-K partial rows (0 with no splits) */
+    int32_t reserved[4];         /* must be 0 */
+} ps_plan_options;
 
 /*
  * Build the packed step's metadata on the host (the Pack stage of
@@ -119,19 +173,22 @@ enum {
  *                                  num_kv_heads; head h reads KV head
  *                                  h / (num_q_heads / num_kv_heads))
  *   pool                           geometry and dtype (pointers unused here)
- *   flags                          PS_PLAN_*
+ *   flags                          PS_PLAN_* (kernel choice | switches)
+ *   options                        NULL or tuning / capacity options
  *
  * Validates: lengths, table width, block ids in [0, num_blocks), no block
- * twice in one table, distinct slots for the new tokens, and no new token
- * written into a block that more than one table references (shared blocks
- * are read-only; tinyserve README "How it works": copy-on-write precedes
- * any write into a shared block). On success *out_plan owns host memory
- * until ps_plan_destroy. num_seqs == 0 gives an empty plan.
+ * twice in one table, and no new token written into a block that more than
+ * one table references (shared blocks are read-only; tinyserve README "How
+ * it works": copy-on-write precedes any write into a shared block). Work
+ * is proportional to the table entries the step covers, not to the pool.
+ * On success *out_plan owns host memory until ps_plan_destroy. num_seqs ==
+ * 0 gives an empty plan.
  */
 ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_computed_tokens,
                        int32_t num_seqs, const int32_t *block_tables,
                        int32_t block_table_stride, int32_t num_q_heads,
-                       const ps_pool *pool, uint32_t flags, ps_plan **out_plan);
+                       const ps_pool *pool, uint32_t flags, const ps_plan_options *options,
+                       ps_plan **out_plan);
 
 /*
  * Device memory the caller must provide: metadata_bytes for
@@ -145,7 +202,9 @@ ps_status ps_plan_sizes(const ps_plan *plan, size_t *metadata_bytes, size_t *wor
  * (metadata_bytes long, 256-byte aligned) on `stream`. The plan remembers
  * metadata_dev; that memory must stay valid, and unchanged, while the plan
  * is used. The host copy stays owned by the plan, so the plan must outlive
- * the copy (synchronise the stream before ps_plan_destroy).
+ * the copy (synchronise the stream before ps_plan_destroy). With
+ * PS_PLAN_FIXED_SHAPE, the next step's plan may be uploaded into the same
+ * buffer once the previous step's work on it is done (same stream).
  */
 ps_status ps_plan_upload(ps_plan *plan, void *metadata_dev, size_t metadata_bytes, void *stream);
 
@@ -167,31 +226,45 @@ ps_status ps_plan_host_arrays(const ps_plan *plan, ps_step_arrays *arrays);
 
 /*
  * What the step costs by definition (algorithmic work, not what a kernel
- * happens to move). KV bytes count each visible (token, KV head) row of
- * K and V once per sequence, shared by the query heads of its group; the
- * "unique" figure counts each physical block once however many tables
- * share it. flops = 4 * head_dim per (query row, visible key): one
- * multiply-add each for q.k and for p.v.
+ * happens to move), and what the planner chose. KV bytes count each
+ * visible (token, KV head) row of K and V once per sequence, shared by the
+ * query heads of its group; the "unique" figure counts each physical block
+ * once however many tables share it. flops = 4 * head_dim per (query row,
+ * visible key): one multiply-add each for q.k and for p.v.
  */
 typedef struct {
     int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, dtype;
     int32_t decode_seqs, prefill_seqs;          /* sequences per attention kernel */
-    int32_t decode_items, prefill_items, merge_items;
+    int32_t decode_items, prefill_items, merge_items;  /* launched (fixed shape: capacities) */
     int32_t decode_row_tiles;                   /* 16-row MFMA tiles per decode work item */
     int64_t kv_bytes_decode, kv_bytes_prefill;  /* logical K+V bytes read */
     int64_t kv_bytes_unique;                    /* distinct physical K+V bytes read */
     int64_t q_bytes, out_bytes, scatter_bytes, table_bytes;
     double flops_decode, flops_prefill;
-    /* Shared prefixes: decode sequences whose tables open with the same
-     * blocks form groups; attention over a group's prefix runs once, in
-     * prefix_items prefill-kernel items (counted in prefill_items) whose
-     * rows come from every member, and merges with each member's own keys
-     * like a key split. step_fused: ps_step runs the scatter inside the
-     * attention launch. */
-    int32_t prefix_groups, prefix_items, step_fused, reserved;
+    /* Shared prefixes (PS_PLAN_SHARED_PREFIX): decode sequences whose
+     * tables open with the same blocks form groups; attention over a
+     * group's prefix runs once, in prefix_items prefill-kernel items
+     * (counted in prefill_items) whose rows come from every member, and
+     * merges with each member's own keys like a key split. step_fused:
+     * ps_step runs the scatter inside the attention launch. */
+    int32_t prefix_groups, prefix_items, step_fused, flags;
+    /* the choices the planner made (options resolved) */
+    int32_t decode_split_keys, prefill_split_keys, decode_waves, mixed_launch;
+    int32_t active_decode_items, active_merge_items;  /* items that do work (fixed shape pads) */
+    int64_t workspace_rows;                     /* split-K partial rows */
+    double plan_us;                             /* host time ps_plan_step took */
 } ps_plan_info;
 
 ps_status ps_plan_get_info(const ps_plan *plan, ps_plan_info *info);
+
+/*
+ * Which attention kernel serves each sequence:
+ * kinds[s] = 0 decode / verify kernel, 1 prefill-chunk kernel, 2 decode
+ * kernel for the keys past a shared prefix whose attention runs in
+ * prefill-kernel items (PS_PLAN_SHARED_PREFIX). kinds holds num_seqs
+ * entries (host memory).
+ */
+ps_status ps_plan_sequence_kernels(const ps_plan *plan, int32_t *kinds, int32_t num_seqs);
 
 void ps_plan_destroy(ps_plan *plan);
 
@@ -221,12 +294,29 @@ ps_status ps_reshape_and_cache(const void *k, const void *v, const int32_t *slot
  * Softmax and accumulation run in fp32; the output is rounded to the pool
  * dtype (round to nearest even).
  *
+ * The plan fixes how the work is cut (which sequence, KV head, query rows
+ * and key range each workgroup covers); the kernels read everything about
+ * a sequence from the call's own device arrays: its first packed row from
+ * query_start_loc[s], its offset c_s from num_computed_tokens[s], its key
+ * count from context_lens[s] (keys at or past it are never read) and every
+ * block id from block_tables[s]. They need not be the arrays
+ * ps_plan_device_arrays returns (any caller-owned copies), but they must
+ * hold the values ps_plan_step derived or was given for this step, with
+ * block ids that may differ (a table pointing at other blocks holding the
+ * same tokens gives the same result). If they hold other values the result
+ * is undefined, but every access stays inside the buffers the call's
+ * sizes describe: a block id outside [0, num_blocks) reads block
+ * num_blocks - 1, a packed row outside [0, num_tokens) is clamped into it.
+ *
  *   q           device [num_tokens, num_q_heads, head_dim], pool dtype
- *   block_tables, query_start_loc, num_computed_tokens, context_lens
- *               device arrays with the contents ps_plan_step derived for
- *               this step (e.g. those of ps_plan_device_arrays)
+ *   block_tables          device [num_seqs, block_table_stride]
+ *   query_start_loc       device [num_seqs + 1]
+ *   num_computed_tokens   device [num_seqs]
+ *   context_lens          device [num_seqs], c_s + n_s
  *   out         device [num_tokens, num_q_heads, head_dim], pool dtype
- *   plan        the uploaded plan of this step; its sizes must match
+ *   plan        the uploaded plan of this step; num_seqs, num_tokens,
+ *               num_q_heads, block_table_stride and the pool geometry must
+ *               be the plan's
  *   workspace   device scratch of at least ps_plan_sizes' workspace_bytes
  *               (256-byte aligned); the call overwrites it
  */

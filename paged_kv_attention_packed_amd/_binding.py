@@ -28,10 +28,12 @@ PS_ERR_HOST_MEMORY = 5
 
 PS_F32, PS_F16, PS_BF16 = 0, 1, 2
 PS_PLAN_DEFAULT, PS_PLAN_ALL_DECODE, PS_PLAN_ALL_PREFILL = 0, 1, 2
+PS_PLAN_SHARED_PREFIX, PS_PLAN_SEPARATE_LAUNCHES, PS_PLAN_FIXED_SHAPE = 4, 8, 16
 
 EXPORTED = [
     "ps_plan_step", "ps_plan_sizes", "ps_plan_upload", "ps_plan_device_arrays",
-    "ps_plan_host_arrays", "ps_plan_get_info", "ps_plan_destroy", "ps_reshape_and_cache",
+    "ps_plan_host_arrays", "ps_plan_get_info", "ps_plan_sequence_kernels", "ps_plan_destroy",
+    "ps_reshape_and_cache",
     "ps_paged_attention", "ps_step", "ps_copy_blocks", "ps_rope_reshape_and_cache", "ps_spec_verify",
     "ps_spec_verify_workspace_bytes", "ps_status_string", "ps_last_error_message", "ps_abi_version",
 ]
@@ -52,6 +54,24 @@ class ps_step_arrays(ctypes.Structure):
                 ("positions", ctypes.c_void_p)]
 
 
+class ps_plan_options(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "decode_split_keys", "prefill_split_keys", "decode_waves", "prefix_min_seqs",
+        "prefix_min_keys", "prefix_slice_keys", "max_seqs", "max_tokens", "max_query_len",
+        "max_decode_items", "max_merge_items", "max_workspace_rows")] + [
+        ("reserved", ctypes.c_int32 * 4)]
+
+
+def plan_options(**kw) -> ps_plan_options:
+    """ps_plan_options with the named fields set (the rest 0 = planner's choice)."""
+    o = ps_plan_options()
+    for k, v in kw.items():
+        if k not in dict(ps_plan_options._fields_) or k == "reserved":
+            raise TypeError(f"unknown plan option {k}")
+        setattr(o, k, int(v))
+    return o
+
+
 class ps_plan_info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_seqs", "num_tokens", "num_q_heads", "num_kv_heads", "head_dim", "dtype",
@@ -60,7 +80,10 @@ class ps_plan_info(ctypes.Structure):
         "kv_bytes_decode", "kv_bytes_prefill", "kv_bytes_unique", "q_bytes", "out_bytes",
         "scatter_bytes", "table_bytes")] + [("flops_decode", ctypes.c_double),
                                             ("flops_prefill", ctypes.c_double)] + [
-        (n, ctypes.c_int32) for n in ("prefix_groups", "prefix_items", "step_fused", "reserved")]
+        (n, ctypes.c_int32) for n in ("prefix_groups", "prefix_items", "step_fused", "flags",
+                                      "decode_split_keys", "prefill_split_keys", "decode_waves",
+                                      "mixed_launch", "active_decode_items", "active_merge_items")] + [
+        ("workspace_rows", ctypes.c_int64), ("plan_us", ctypes.c_double)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -82,7 +105,8 @@ _sz = ctypes.c_size_t
 
 lib.ps_plan_step.restype = ctypes.c_int32
 lib.ps_plan_step.argtypes = [_i32p, _i32p, ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32,
-                             ctypes.POINTER(ps_pool), ctypes.c_uint32, ctypes.POINTER(_vp)]
+                             ctypes.POINTER(ps_pool), ctypes.c_uint32, ctypes.POINTER(ps_plan_options),
+                             ctypes.POINTER(_vp)]
 lib.ps_plan_sizes.restype = ctypes.c_int32
 lib.ps_plan_sizes.argtypes = [_vp, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
 lib.ps_plan_upload.restype = ctypes.c_int32
@@ -93,6 +117,8 @@ lib.ps_plan_host_arrays.restype = ctypes.c_int32
 lib.ps_plan_host_arrays.argtypes = [_vp, ctypes.POINTER(ps_step_arrays)]
 lib.ps_plan_get_info.restype = ctypes.c_int32
 lib.ps_plan_get_info.argtypes = [_vp, ctypes.POINTER(ps_plan_info)]
+lib.ps_plan_sequence_kernels.restype = ctypes.c_int32
+lib.ps_plan_sequence_kernels.argtypes = [_vp, _i32p, ctypes.c_int32]
 lib.ps_plan_destroy.restype = None
 lib.ps_plan_destroy.argtypes = [_vp]
 lib.ps_reshape_and_cache.restype = ctypes.c_int32
@@ -175,7 +201,7 @@ class Plan:
 
 
 def ps_plan_step(q_lens, num_computed_tokens, block_tables, num_q_heads: int, pool: ps_pool,
-                 flags: int = PS_PLAN_DEFAULT) -> Plan:
+                 flags: int = PS_PLAN_DEFAULT, options: Optional[ps_plan_options] = None) -> Plan:
     ql = np.ascontiguousarray(q_lens, dtype=np.int32)
     nc = np.ascontiguousarray(num_computed_tokens, dtype=np.int32)
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
@@ -185,7 +211,8 @@ def ps_plan_step(q_lens, num_computed_tokens, block_tables, num_q_heads: int, po
     out = _vp()
     _check(lib.ps_plan_step(ql.ctypes.data_as(_i32p), nc.ctypes.data_as(_i32p), len(ql),
                             bt.ctypes.data_as(_i32p), stride, num_q_heads,
-                            ctypes.byref(pool), flags, ctypes.byref(out)))
+                            ctypes.byref(pool), flags, ctypes.byref(options) if options is not None else None,
+                            ctypes.byref(out)))
     return Plan(out.value)
 
 
@@ -228,6 +255,13 @@ def ps_plan_get_info(plan: Plan) -> dict:
     info = ps_plan_info()
     _check(lib.ps_plan_get_info(plan.handle, ctypes.byref(info)))
     return info.as_dict()
+
+
+def ps_plan_sequence_kernels(plan: Plan, num_seqs: int) -> np.ndarray:
+    """Per sequence: 0 decode kernel, 1 prefill kernel, 2 decode after a shared prefix."""
+    kinds = np.zeros(max(num_seqs, 1), dtype=np.int32)
+    _check(lib.ps_plan_sequence_kernels(plan.handle, kinds.ctypes.data_as(_i32p), num_seqs))
+    return kinds[:num_seqs]
 
 
 def ps_reshape_and_cache(k, v, slot_mapping, num_tokens: int, pool: ps_pool, stream=None):

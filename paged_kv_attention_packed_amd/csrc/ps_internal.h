@@ -11,7 +11,7 @@
 // kv_head * g + r % g (g = num_q_heads / num_kv_heads), so the g heads that
 // read the same K/V share every K/V load.
 struct ps_item {
-    int32_t seq;
+    int32_t seq;         // sequence index; < 0: an idle item (fixed-shape padding) that exits
     int32_t kv_head;
     int32_t row_begin;   // first packed row
     int32_t row_end;     // one past the last packed row
@@ -19,10 +19,6 @@ struct ps_item {
     int32_t key_end;     // one past the last key position (<= context length)
     int32_t partial_row; // -1: write the output; else first workspace row of this item's partials
     int32_t flags;       // PS_ITEM_* bits
-    // Copies of the sequence's offsets, so that a workgroup's first
-    // dependent loads need only the item.
-    int32_t q_start;      // query_start_loc[seq]
-    int32_t num_computed; // num_computed_tokens[seq]
     // Decode items walk their 32-key tiles starting at tile `rot` (mod the
     // tile count): items that share prefix blocks then do not request the
     // same lines at the same time (softmax order is free). Prefill: 0.
@@ -30,6 +26,7 @@ struct ps_item {
     // Gathered items (PS_ITEM_GATHERED): which slice of the shared prefix's
     // keys the item covers; its partials go to a row's dest + split * stride.
     int32_t split;
+    int32_t pad[2];
 };
 static_assert(sizeof(ps_item) == 48, "ps_item layout");
 // The one item per (sequence, KV head) that holds the sequence's last keys
@@ -41,26 +38,27 @@ constexpr int32_t PS_ITEM_WRITES_NEW = 1;
 // every key of its range is visible to every row.
 constexpr int32_t PS_ITEM_GATHERED = 2;
 
-// One gathered row: which query row it reads and where its partial goes.
+// One gathered row: which sequence and packed row it is, and where its
+// partial goes.
 struct ps_row {
-    int32_t q_row;   // t * num_q_heads + h: the row of q (and of out)
+    int32_t seq;     // the row's sequence
+    int32_t row;     // packed row within the sequence's KV head (token r / g, head j g + r % g)
     int32_t dest;    // workspace row of the first prefix slice's partial
     int32_t stride;  // rows from one slice's partial to the next
-    int32_t pad;
 };
 static_assert(sizeof(ps_row) == 16, "ps_row layout");
 
 // A chunk of rows (at most ps_merge_rows(D)) of one set of split-K
 // partials, merged into the output by one workgroup of the merge kernel.
 struct ps_merge {
-    int32_t seq;
+    int32_t seq;          // < 0: idle (fixed-shape padding)
     int32_t kv_head;
     int32_t row_begin;
     int32_t row_end;
     int32_t partial_row; // split i's row r is partial_row + i * split_stride + (r - row_begin)
     int32_t num_splits;
     int32_t split_stride; // rows of each split's partial block
-    int32_t q_start;      // query_start_loc[seq]
+    int32_t pad;
 };
 // rows one merge workgroup covers: 256 threads, each 4 elements of a row
 inline int ps_merge_rows(int head_dim) { return 1024 / head_dim; }
@@ -113,6 +111,8 @@ struct ps_attn_launch {
     void *out;
     const void *pool_k;
     const void *pool_v;
+    // the call's per-sequence arrays: the kernels read every sequence's
+    // offsets and block ids here
     const int32_t *block_tables;
     const int32_t *query_start_loc;
     const int32_t *num_computed;
@@ -120,7 +120,13 @@ struct ps_attn_launch {
     const ps_item *decode_items;
     const ps_item *prefill_items;
     const ps_merge *merges;
-    const int32_t *decode_head;   // [n_decode][2 * PS_DEC_HEAD_TILES] block ids
+    // [n_decode][2 * PS_DEC_HEAD_TILES] block ids of each decode item's
+    // first tiles, copied from the plan's table. head_ok: the call reads
+    // the plan's own uploaded table, so these are that table's entries
+    // and a wave's first tiles need no table read; otherwise they are
+    // never used.
+    const int32_t *decode_head;
+    int32_t head_ok;
     const ps_row *row_map;        // rows of the gathered (shared-prefix) items
     float *ws_m;
     float *ws_l;
@@ -128,6 +134,7 @@ struct ps_attn_launch {
     int64_t layer_offset;   // elements from pool start to this layer
     int32_t bt_stride;
     int32_t num_blocks;
+    int32_t num_tokens;     // packed rows of q / out: row indexes are clamped below it
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t head_dim;
@@ -135,6 +142,7 @@ struct ps_attn_launch {
     int32_t n_decode, n_prefill, n_merge;
     int32_t decode_row_tiles;
     int32_t decode_waves;   // waves per decode workgroup (4, 8 or 16)
+    int32_t mixed;          // decode and prefill items share one launch
     float scale_log2;       // softmax scale * log2(e)
     // g = num_q_heads / num_kv_heads, and r / g for 0 <= r < 2^31 as
     // (r * g_magic) >> g_shift (see ps_group_divisor)
@@ -217,7 +225,6 @@ int ps_launch_scatter(const void *k, const void *v, const int32_t *slot_mapping,
                       int32_t num_tokens, const ps_pool *pool, void *stream);
 int ps_launch_attention(const ps_attn_launch &a, void *stream);
 int ps_prefill_rows(int dtype);  // packed rows per prefill work item
-bool ps_mixed_launch(int dtype);  // decode and prefill items share one launch
 int ps_launch_copy_blocks(const ps_pool *src, const ps_pool *dst, const int32_t *src_blocks,
                           const int32_t *dst_blocks, int32_t num_pairs, void *stream);
 int ps_launch_rope_cache(const ps_rope_launch &a, void *stream);

@@ -238,6 +238,28 @@ __device__ inline int div_g(const ps_attn_launch &a, int r) {
     return (int)(((uint64_t)(uint32_t)r * a.g_magic) >> a.g_shift);
 }
 
+// Packed token `local` of a sequence whose first token is qs0, clamped
+// into [0, num_tokens): with arrays that keep the call's contract the
+// clamp changes nothing; with others every access stays inside q, out, k
+// and v.
+__device__ inline int tok_index(const ps_attn_launch &a, int qs0, int local) {
+    return min(max(qs0 + local, 0), a.num_tokens - 1);
+}
+
+// A block id read from the call's table, clamped into the pool.
+__device__ inline int64_t clamp_blk(const ps_attn_launch &a, int32_t id) {
+    return (int64_t)min((uint32_t)id, (uint32_t)(a.num_blocks - 1));
+}
+
+// What a work item needs about its sequence, from the call's own arrays:
+// first packed row, tokens already in the pool, context length.
+struct SeqInfo {
+    int qs0, nc, ctx;
+};
+__device__ inline SeqInfo seq_info(const ps_attn_launch &a, int s) {
+    return SeqInfo{a.query_start_loc[s], a.num_computed[s], a.context_lens[s]};
+}
+
 // Which query row a lane's packed row stands for, its visibility limit and
 // its Q fragment.
 // A row past the item's end (r >= row_end) loads the item's last row
@@ -246,16 +268,17 @@ __device__ inline int div_g(const ps_attn_launch &a, int r) {
 // unconditionally keeps the loads out of a branch whose other side would
 // write the same registers, which would make the compiler wait for them
 // (and for everything issued before them) on the spot.
+// A row sees key tau iff tau <= nc + (its token) and tau < ctx.
 template <class DT, int D>
 __device__ inline void load_q_row(const ps_attn_launch &a, int r, int row_end, int g, int kv_head,
-                                  int qs0, int nc, int q4, u32x4 (&qf)[Geo<DT, D>::KU4], int &lim) {
+                                  const SeqInfo &si, int q4, u32x4 (&qf)[Geo<DT, D>::KU4], int &lim) {
     const bool ok = r < row_end;
     const int rr = ok ? r : row_end - 1;
     const int tok = div_g(a, rr);
     const int h = kv_head * g + (rr - tok * g);
-    lim = ok ? nc + tok : -1;
+    lim = ok ? min(si.nc + tok, si.ctx - 1) : -1;
     const typename DT::T *qp =
-        static_cast<const typename DT::T *>(a.q) + ((int64_t)(qs0 + tok) * a.num_q_heads + h) * D;
+        static_cast<const typename DT::T *>(a.q) + ((int64_t)tok_index(a, si.qs0, tok) * a.num_q_heads + h) * D;
 #pragma unroll
     for (int u = 0; u < Geo<DT, D>::KU4; ++u)
         qf[u] = *reinterpret_cast<const u32x4 *>(qp + (u * 4 + q4) * (16 / DT::ELT));
@@ -399,24 +422,30 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     const int2 hid0 = head[wave];
     const int2 hid1 = head[min(wave + NW, PS_DEC_HEAD_TILES - 1)];
     asm volatile("" ::"s"(it.seq), "s"(it.kv_head), "s"(it.row_begin), "s"(it.row_end), "s"(it.key_begin),
-                 "s"(it.key_end), "s"(it.partial_row), "s"(it.flags), "s"(it.q_start), "s"(it.num_computed),
-                 "s"(it.rot), "s"(hid0.x), "s"(hid0.y), "s"(hid1.x), "s"(hid1.y), "s"(a.pool_k), "s"(a.pool_v),
-                 "s"(a.layer_offset), "s"(a.block_tables), "s"(a.bt_stride), "s"(a.q), "s"(a.k_new),
-                 "s"(a.v_new), "s"(a.num_kv_heads), "s"(a.g), "s"(a.g_magic));
+                 "s"(it.key_end), "s"(it.partial_row), "s"(it.flags), "s"(it.rot), "s"(hid0.x), "s"(hid0.y),
+                 "s"(hid1.x), "s"(hid1.y), "s"(a.pool_k), "s"(a.pool_v), "s"(a.layer_offset),
+                 "s"(a.block_tables), "s"(a.bt_stride), "s"(a.q), "s"(a.k_new), "s"(a.v_new),
+                 "s"(a.num_kv_heads), "s"(a.g), "s"(a.g_magic), "s"(a.query_start_loc), "s"(a.num_computed),
+                 "s"(a.context_lens), "s"(a.head_ok));
+    if (it.seq < 0) return;   // an idle item of a fixed-shape launch
     const int c = lane & 15, q4 = lane >> 4;
     const int s = it.seq, j = it.kv_head;
     const int g = a.g;
-    const int qs0 = it.q_start, nc = it.num_computed;
+    // the sequence's offsets, from the call's arrays
+    const SeqInfo si = seq_info(a, s);
+    const int qs0 = si.qs0, nc = max(si.nc, 0);
     const int32_t *bt = a.block_tables + (int64_t)s * a.bt_stride;
     const int64_t rs = (int64_t)a.num_kv_heads * D;  // elements from one slot to the next
     const T *kp = static_cast<const T *>(a.pool_k) + a.layer_offset + (int64_t)j * D;
     const T *vp = static_cast<const T *>(a.pool_v) + a.layer_offset + (int64_t)j * D;
     const int kb = it.key_begin, ke = it.key_end;
-    // fused scatter: this step's keys (positions nc..) come from the inputs
+    // fused scatter: this step's keys (positions nc..) come from the inputs,
+    // key position p from packed token qs0 + p - nc
     const bool fused = a.fuse_scatter != 0;
-    const T *kn = fused ? static_cast<const T *>(a.k_new) + (int64_t)j * D + (int64_t)(qs0 - nc) * rs : kp;
-    const T *vn = fused ? static_cast<const T *>(a.v_new) + (int64_t)j * D + (int64_t)(qs0 - nc) * rs : vp;
+    const T *kn = static_cast<const T *>(fused ? a.k_new : a.pool_k) + (int64_t)j * D;
+    const T *vn = static_cast<const T *>(fused ? a.v_new : a.pool_v) + (int64_t)j * D;
     const int new_lo = fused ? nc : INT32_MAX;   // keys in [new_lo, ke) are read from kn / vn
+    auto new_row = [&](int pos) { return (int64_t)tok_index(a, qs0, pos - nc); };
 
     // The item's block ids go to LDS once: every tile after a wave's first
     // reads its two ids there instead of waiting on a scalar load from the
@@ -446,14 +475,15 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     // adds no load latency to the item's end.
     constexpr int WPR = D * ELT / 16;   // 16-byte words per head row
     const bool writer = fused && (it.flags & PS_ITEM_WRITES_NEW);
-    const int sc_units = writer ? 2 * (ke - nc) * WPR : 0;
+    const int n_new = max(ke - nc, 0);
+    const int sc_units = writer ? 2 * n_new * WPR : 0;
     const int64_t rw16 = rs * ELT / 16;   // 16-byte words from one slot (or token) to the next
     auto sc_word = [&](int w, const u32x4 *&src, int &i, int &cw, int &which) {
-        which = w >= (ke - nc) * WPR;   // K words first, then V (w < sc_units)
-        const int r2 = w - which * (ke - nc) * WPR;
+        which = w >= n_new * WPR;   // K words first, then V (w < sc_units)
+        const int r2 = w - which * n_new * WPR;
         i = r2 / WPR;
         cw = r2 - i * WPR;
-        src = reinterpret_cast<const u32x4 *>(which ? vn : kn) + (int64_t)(nc + i) * rw16 + cw;
+        src = reinterpret_cast<const u32x4 *>(which ? vn : kn) + (int64_t)tok_index(a, qs0, i) * rw16 + cw;
     };
     u32x4 sc_data = {0u, 0u, 0u, 0u};
     int32_t sc_slot = -1;
@@ -462,7 +492,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
         const u32x4 *src;
         int i;
         sc_word(tid, src, i, sc_cw, sc_which);
-        sc_slot = a.slot_mapping[qs0 + i];
+        sc_slot = a.slot_mapping[tok_index(a, qs0, i)];
         sc_data = *src;
     }
 
@@ -470,7 +500,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     int lim[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
-        load_q_row<DT, D>(a, it.row_begin + rt * 16 + c, it.row_end, g, j, qs0, nc, q4, qf[rt], lim[rt]);
+        load_q_row<DT, D>(a, it.row_begin + rt * 16 + c, it.row_end, g, j, si, q4, qf[rt], lim[rt]);
 
     float m[RT], l[RT];
     f32x4 o[RT][NT];
@@ -507,15 +537,15 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
         int64_t blk0, blk1;
         if constexpr (decltype(from_lds)::value) {
             const int li = (k0 - kb) >> 4;
-            blk0 = __builtin_amdgcn_readfirstlane(sbt[li]);
-            blk1 = has1 ? __builtin_amdgcn_readfirstlane(sbt[li + 1]) : blk0;
-        } else if (t < PS_DEC_HEAD_TILES) {   // t is wave or wave + NW
+            blk0 = clamp_blk(a, __builtin_amdgcn_readfirstlane(sbt[li]));
+            blk1 = has1 ? clamp_blk(a, __builtin_amdgcn_readfirstlane(sbt[li + 1])) : blk0;
+        } else if (a.head_ok && t < PS_DEC_HEAD_TILES) {   // t is wave or wave + NW
             const int2 ids = t == wave ? hid0 : hid1;
             blk0 = ids.x;
             blk1 = ids.y;
         } else {
-            blk0 = bt[k0 >> 4];
-            blk1 = has1 ? (int64_t)bt[(k0 >> 4) + 1] : blk0;
+            blk0 = clamp_blk(a, bt[k0 >> 4]);
+            blk1 = has1 ? clamp_blk(a, bt[(k0 >> 4) + 1]) : blk0;
         }
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
@@ -536,15 +566,15 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
                 for (int i = 0; i < 4; ++i) load_words<VW>(vb_pool + voff[i], vr[buf][sb * 4 + i]);
             } else {
                 // the block holds keys of this step: rows in [new_lo, ke)
-                // come from k_new / v_new, whose token rows have the same
-                // stride as pool slots
-                const char *kb_new = knew + (int64_t)kbk * rsb, *vb_new = vnew + (int64_t)kbk * rsb;
+                // come from k_new / v_new (key position p is packed token
+                // qs0 + p - nc, whose row has the same stride as a pool slot)
                 if (sb == 0 || has1) {
                     const int pos = kbk + c;
-                    const char *base = pos >= new_lo && pos < ke ? kb_new : kb_pool;
+                    const char *src = pos >= new_lo && pos < ke ? knew + new_row(pos) * rsb + 16 * q4
+                                                                : kb_pool + koff;
 #pragma unroll
                     for (int u = 0; u < KU4; ++u)
-                        kf[buf][sb][u] = *reinterpret_cast<const u32x4 *>(base + koff + 64 * u);
+                        kf[buf][sb][u] = *reinterpret_cast<const u32x4 *>(src + 64 * u);
                 } else {
 #pragma unroll
                     for (int u = 0; u < KU4; ++u) kf[buf][sb][u] = u32x4{0u, 0u, 0u, 0u};
@@ -552,8 +582,9 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int pos = kbk + 4 * q4 + i;
-                    const char *base = pos >= new_lo && pos < ke ? vb_new : vb_pool;
-                    load_words<VW>(base + voff[i], vr[buf][sb * 4 + i]);
+                    const char *src = pos >= new_lo && pos < ke ? vnew + new_row(pos) * rsb + EPL * c * ELT
+                                                                : vb_pool + voff[i];
+                    load_words<VW>(src, vr[buf][sb * 4 + i]);
                 }
             }
         }
@@ -561,7 +592,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
 
     // keys below vis_all are visible to every row of the item (the first
     // row's query sits at position nc + row_begin / g)
-    const int vis_all = min(ke, nc + div_g(a, it.row_begin) + 1);
+    const int vis_all = min(min(ke, si.ctx), nc + div_g(a, it.row_begin) + 1);
     auto compute_tile = [&](auto bufc, int k0) {
         constexpr int buf = decltype(bufc)::value;
         float pv[RT][8];
@@ -683,7 +714,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
                          slot_lds + i * 1024);
             } else {
                 const int pos = k0 + rr;
-                const T *src = pos >= new_lo && pos < ke ? (kv ? vn : kn) + (int64_t)pos * rs + chunk
+                const T *src = pos >= new_lo && pos < ke ? (kv ? vn : kn) + new_row(pos) * rs + chunk
                                                          : pool + (blk * 16 + (rr & 15)) * rs + chunk;
                 dma16(src, slot + i * 1024);
             }
@@ -720,12 +751,12 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
             // the wave's second tile: ids from the head (or the table)
             const int t1 = ti + NW, k1 = key0(t1);
             int64_t b0, b1;
-            if (t1 < PS_DEC_HEAD_TILES) {
+            if (a.head_ok && t1 < PS_DEC_HEAD_TILES) {
                 b0 = hid1.x;
                 b1 = hid1.y;
             } else {
-                b0 = bt[k1 >> 4];
-                b1 = k1 + 16 < ke ? (int64_t)bt[(k1 >> 4) + 1] : b0;
+                b0 = clamp_blk(a, bt[k1 >> 4]);
+                b1 = k1 + 16 < ke ? clamp_blk(a, bt[(k1 >> 4) + 1]) : b0;
             }
             dma_tile(k1, b0, b1);
         }
@@ -742,8 +773,8 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
                 if (ti + NW < ntiles) {
                     const int kn2 = key0(ti + NW);
                     const int li = (kn2 - kb) >> 4;
-                    const int64_t b0 = __builtin_amdgcn_readfirstlane(sbt[li]);
-                    const int64_t b1 = kn2 + 16 < ke ? (int64_t)__builtin_amdgcn_readfirstlane(sbt[li + 1]) : b0;
+                    const int64_t b0 = clamp_blk(a, __builtin_amdgcn_readfirstlane(sbt[li]));
+                    const int64_t b1 = kn2 + 16 < ke ? clamp_blk(a, __builtin_amdgcn_readfirstlane(sbt[li + 1])) : b0;
                     dma_tile(kn2, b0, b1);
                 }
             }
@@ -774,7 +805,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
             const u32x4 *src;
             int i, cw, which;
             sc_word(w, src, i, cw, which);
-            const int32_t slot = a.slot_mapping[qs0 + i];
+            const int32_t slot = a.slot_mapping[tok_index(a, qs0, i)];
             if ((uint32_t)slot >= (uint32_t)a.num_slots) continue;
             (which ? pv : pk)[(int64_t)slot * rw16 + cw] = *src;
         }
@@ -827,7 +858,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     if (it.partial_row < 0) {
         const int tok = div_g(a, r);
         const int h = j * g + (r - tok * g);
-        T *op = static_cast<T *>(a.out) + ((int64_t)(qs0 + tok) * a.num_q_heads + h) * D + d0;
+        T *op = static_cast<T *>(a.out) + ((int64_t)tok_index(a, qs0, tok) * a.num_q_heads + h) * D + d0;
         const float inv = 1.f / L;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) op[e] = cvt_out(acc[e] * inv, DT{});
@@ -938,7 +969,10 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
     const int c = lane & 15, q4 = lane >> 4;
     const int s = it.seq, j = it.kv_head;
     const int g = a.g;
-    const int qs0 = it.q_start, nc = it.num_computed;
+    // the sequence's offsets, from the call's arrays (a gathered item's
+    // rows name their own sequences)
+    const SeqInfo si = seq_info(a, s);
+    const int qs0 = si.qs0, nc = si.nc;
     const int32_t *bt = a.block_tables + (int64_t)s * a.bt_stride;
     const int64_t rs = (int64_t)a.num_kv_heads * D;
     const T *kp = static_cast<const T *>(a.pool_k) + a.layer_offset + (int64_t)j * D;
@@ -955,8 +989,9 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
     // every key of its range is visible to all of them.
     const bool gathered = (it.flags & PS_ITEM_GATHERED) != 0;
     constexpr int kAllVisible = INT32_MAX / 2;
-    const int lim_lo = gathered ? kAllVisible : nc + div_g(a, wr0);      // smallest visibility limit among the wave's rows
-    const int lim_hi = gathered ? kAllVisible : nc + div_g(a, wr_last);  // largest
+    // smallest and largest visibility limits among the wave's rows
+    const int lim_lo = gathered ? kAllVisible : min(nc + div_g(a, wr0), si.ctx - 1);
+    const int lim_hi = gathered ? kAllVisible : min(nc + div_g(a, wr_last), si.ctx - 1);
 
 
     // 16-bit data: o carries one more tile, the row sums of P, formed on
@@ -989,10 +1024,10 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
     auto issue_tile = [&](auto stagec, int k0, IdVec ids) {
         uint8_t *const ring = stage(stagec);
         int64_t blk[NSB];
-        blk[0] = __builtin_amdgcn_readfirstlane(ids[0]);
+        blk[0] = clamp_blk(a, __builtin_amdgcn_readfirstlane(ids[0]));
 #pragma unroll
         for (int b = 1; b < NSB; ++b)
-            blk[b] = (k0 + 16 * b < ke) ? (int64_t)__builtin_amdgcn_readfirstlane(ids[b]) : blk[0];
+            blk[b] = (k0 + 16 * b < ke) ? clamp_blk(a, __builtin_amdgcn_readfirstlane(ids[b])) : blk[0];
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int r0 = (i * RPI) % TK;  // first key row of instruction i (compile-time)
@@ -1034,20 +1069,26 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
     if (!gathered) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-            load_q_row<DT, D>(a, wr0 + rt * 16 + c, it.row_end, g, j, qs0, nc, q4, qf[rt], lim[rt]);
+            load_q_row<DT, D>(a, wr0 + rt * 16 + c, it.row_end, g, j, si, q4, qf[rt], lim[rt]);
     } else {
         // (as in load_q_row: a row past the end reads the last row's map
         // entry and query, unconditionally, and is never stored); all map
-        // entries first, then the queries they name
+        // entries first, then their sequences' first rows, then the
+        // queries they name
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int r = wr0 + rt * 16 + c;
             grow[rt] = a.row_map[it.partial_row + (r < it.row_end ? r : it.row_end - 1)];
             lim[rt] = r < it.row_end ? kAllVisible : -1;
         }
+        int gqs[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) gqs[rt] = a.query_start_loc[grow[rt].seq];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const T *qp = static_cast<const T *>(a.q) + (int64_t)grow[rt].q_row * D;
+            const int tok = div_g(a, grow[rt].row);
+            const int h = j * g + (grow[rt].row - tok * g);
+            const T *qp = static_cast<const T *>(a.q) + ((int64_t)tok_index(a, gqs[rt], tok) * a.num_q_heads + h) * D;
 #pragma unroll
             for (int u = 0; u < KU4; ++u) qf[rt][u] = *reinterpret_cast<const u32x4 *>(qp + (u * 4 + q4) * (16 / ELT));
         }
@@ -1302,7 +1343,7 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
         if (r >= it.row_end) continue;
         const int tok = div_g(a, r);
         const int h = j * g + (r - tok * g);
-        uint8_t *dst = static_cast<uint8_t *>(a.out) + (((int64_t)(qs0 + tok) * a.num_q_heads + h) * D) * ELT;
+        uint8_t *dst = static_cast<uint8_t *>(a.out) + (((int64_t)tok_index(a, qs0, tok) * a.num_q_heads + h) * D) * ELT;
         reinterpret_cast<u32x4 *>(dst)[ch] = *reinterpret_cast<const u32x4 *>(sob + row * D * ELT + ch * 16);
     }
 }
@@ -1369,6 +1410,8 @@ template <class DT, int D>
 __global__ __launch_bounds__(256) void ps_merge_kernel(const ps_attn_launch a) {
     using T = typename DT::T;
     const ps_merge mg = a.merges[blockIdx.x];
+    if (mg.seq < 0) return;   // an idle merge of a fixed-shape launch
+    const int qs0 = a.query_start_loc[mg.seq];
     const int row = threadIdx.x / (D / 4), d0 = (threadIdx.x % (D / 4)) * 4;
     const int r = mg.row_begin + row;
     if (r >= mg.row_end) return;
@@ -1413,7 +1456,7 @@ __global__ __launch_bounds__(256) void ps_merge_kernel(const ps_attn_launch a) {
     }
     const int tok = div_g(a, r);
     const int h = mg.kv_head * g + (r - tok * g);
-    T *op = static_cast<T *>(a.out) + ((int64_t)(mg.q_start + tok) * a.num_q_heads + h) * D + d0;
+    T *op = static_cast<T *>(a.out) + ((int64_t)tok_index(a, qs0, tok) * a.num_q_heads + h) * D + d0;
     const float inv = 1.f / L;
 #pragma unroll
     for (int e = 0; e < 4; ++e) op[e] = cvt_out(acc[e] * inv, DT{});
@@ -1422,56 +1465,19 @@ __global__ __launch_bounds__(256) void ps_merge_kernel(const ps_attn_launch a) {
 // ---------------------------------------------------------------------------
 // Launchers
 
-// Prefill kernel shape (tuning knob, PS_PREFILL_VARIANT): 0 = 64-key tiles
-// in a two-stage ring, 32 rows per wave at two waves per SIMD (default for
-// 16-bit data); 1 = 32-key tiles in a three-stage ring; 2 = 32-key tiles in
-// a two-stage ring; 3 = 64-key tiles, 32 rows per wave at one wave per SIMD
-// (512 registers). fp32 rows always take 32-key tiles in two stages. (64
-// rows per wave, RPW = 64, halves the LDS reads per MFMA but spills at
-// head_dim 128 and measured slower.)
-int prefill_variant() {
-    static const int v = [] {
-        const char *e = std::getenv("PS_PREFILL_VARIANT");
-        return e ? std::atoi(e) : 0;
-    }();
-    return v;
-}
-
 }  // namespace psk
 
-// Packed rows per prefill work item for the kernel shape the launcher will
-// pick (the planner cuts items to match).
-int ps_prefill_rows(int dtype) {
-    (void)dtype;  // every shape launched today takes 32 rows per wave
-    return PS_PRE_WAVES * 32;
-}
-
-namespace psk {
-bool mixed_launch();
-}
-
-// Whether a step of this dtype with both decode and prefill items runs them
-// in one launch (the planner sizes prefill key slices for it).
-bool ps_mixed_launch(int dtype) {
-    return dtype != PS_F32 && psk::prefill_variant() == 0 && psk::mixed_launch();
-}
-
 namespace psk {
 
-// Decode and prefill items in one launch when a step has both (tuning knob,
-// PS_MIXED=0 launches them one after the other).
-bool mixed_launch() {
-    static const bool v = [] {
-        const char *e = std::getenv("PS_MIXED");
-        return !(e && std::atoi(e) == 0);
-    }();
-    return v;
-}
-
+// Launches of one attention call. Kernel shapes: decode items of one row
+// tile run 4, 8 or 16 waves (the plan's choice), of two row tiles 4 waves;
+// prefill items 4 waves of 32 rows over 64-key tiles (32-key tiles for
+// fp32) in a two-stage LDS ring; a step with both kinds runs them in one
+// launch unless the plan asks for two.
 template <class DT, int D>
 hipError_t launch_attention_t(const ps_attn_launch &a, hipStream_t st) {
     if constexpr (DT::ELT == 2) {
-        if (a.n_decode > 0 && a.n_prefill > 0 && prefill_variant() == 0 && mixed_launch()) {
+        if (a.n_decode > 0 && a.n_prefill > 0 && a.mixed) {
             const dim3 grid(a.n_decode + a.n_prefill), block(256);
             if (a.decode_row_tiles == 2)
                 hipLaunchKernelGGL((ps_mixed_kernel<DT, D, 2>), grid, block, 0, st, a);
@@ -1496,23 +1502,10 @@ hipError_t launch_attention_t(const ps_attn_launch &a, hipStream_t st) {
     }
     if (a.n_prefill > 0) {
         const dim3 grid(a.n_prefill), block(256);
-        if constexpr (DT::ELT == 4) {
+        if constexpr (DT::ELT == 4)
             hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 2, 32>), grid, block, 0, st, a);
-        } else {
-            switch (prefill_variant()) {
-                case 1:
-                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 3, 32>), grid, block, 0, st, a);
-                    break;
-                case 2:
-                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 2, 32>), grid, block, 0, st, a);
-                    break;
-                case 3:
-                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE, 1, 2, 32>), grid, block, 0, st, a);
-                    break;
-                default:
-                    hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE, 2, 2, 32>), grid, block, 0, st, a);
-            }
-        }
+        else
+            hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE, 2, 2, 32>), grid, block, 0, st, a);
     }
     if (a.n_merge > 0)
         hipLaunchKernelGGL((ps_merge_kernel<DT, D>), dim3(a.n_merge), dim3(256), 0, st, a);

@@ -1,15 +1,20 @@
 // Host metadata builder for one packed step: validation, the packed batch's
 // index arrays, the attention kernels' work lists and the step's
 // algorithmic byte / FLOP counts. Pure host code: no HIP call happens here
-// except in ps_plan_upload.
+// except in ps_plan_upload and the launches of the attention entry points.
 //
 // The packed layout follows PageServe "01 Scheduler loop" (Pack: one
 // [1, T] batch, explicit positions, a slot mapping per token, no padding)
 // and "03 Paged KV cache" (slot = block_table[pos / 16] * 16 + pos % 16).
+//
+// Every choice the planner makes comes from its arguments (flags and
+// options) and is recorded in ps_plan_info; nothing is read from the
+// process environment.
 
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -21,15 +26,17 @@ struct ps_plan {
     int32_t S = 0, T = 0, Hq = 0, Hkv = 0, D = 0, dtype = 0;
     int32_t num_blocks = 0, num_layers = 0, bt_stride = 0;
     uint32_t flags = 0;
-    int32_t dec_rt = 1;
-    int64_t ws_rows = 0;
-    int32_t n_dec = 0, n_pre = 0, n_mrg = 0;
+    int32_t dec_rt = 1, dec_waves = 4;
+    bool mixed = false, fixed = false;
+    int64_t ws_rows = 0;                 // workspace layout rows (fixed shape: the capacity)
+    int32_t rows_cap = 0;                // packed tokens q / out hold (fixed shape: max_tokens)
+    int32_t n_dec = 0, n_pre = 0, n_mrg = 0;   // launched items (fixed shape: capacities)
+    int32_t n_gathered = 0;              // prefill items of the shared-prefix pass
     // the metadata blob, laid out exactly as it is copied to the device
     std::vector<uint8_t> blob;
     size_t off_qsl = 0, off_nc = 0, off_ctx = 0, off_slot = 0, off_pos = 0, off_bt = 0;
-    size_t off_dhead = 0, off_rmap = 0;
-    int32_t n_gathered = 0;   // prefill items of the shared-prefix pass
-    size_t off_dec = 0, off_pre = 0, off_mrg = 0;
+    size_t off_dec = 0, off_pre = 0, off_mrg = 0, off_dhead = 0, off_rmap = 0;
+    std::vector<int32_t> kinds;          // per sequence: 0 decode, 1 prefill, 2 decode after a shared prefix
     void *dev = nullptr;
     ps_plan_info info{};
 
@@ -46,24 +53,10 @@ int elt_bytes(int dtype) { return dtype == PS_F32 ? 4 : 2; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
-int64_t env_int(const char *name, int64_t dflt) {
-    const char *s = std::getenv(name);
-    if (!s || !*s) return dflt;
-    char *end = nullptr;
-    long long v = std::strtoll(s, &end, 10);
-    return (end && *end == 0 && v > 0) ? (int64_t)v : dflt;
-}
-
-// A switch read from the environment: unset or empty gives dflt, "0" off.
-bool env_on(const char *name, bool dflt) {
-    const char *s = std::getenv(name);
-    if (!s || !*s) return dflt;
-    return std::strcmp(s, "0") != 0;
-}
-
-// Split [0, kmax) into near-equal pieces of about `target` keys, each a
-// multiple of `align` long except possibly the last. The split set depends
-// only on logical lengths, so physical placement never changes results.
+// Split [0, kmax) into near-equal pieces of at most `target` keys, each a
+// multiple of `align` long except possibly the last (target a multiple of
+// align). The split set depends only on logical lengths, so physical
+// placement never changes results.
 void key_splits(int64_t kmax, int64_t target, int64_t align, std::vector<int64_t> &bounds) {
     bounds.clear();
     int64_t n = std::max<int64_t>(1, ceil_div(kmax, target));
@@ -72,19 +65,137 @@ void key_splits(int64_t kmax, int64_t target, int64_t align, std::vector<int64_t
     for (int64_t i = 0; i <= n; ++i) bounds.push_back(std::min(kmax, i * len));
 }
 
+// Marks on the physical blocks a step's tables cover. The mark of block id
+// is ((s + 1) << 6) | shared << 5 | n: the last sequence s that listed it
+// (a block twice in one table is an error), whether more than one table
+// lists it, and the most tokens n any of them reads from it. Marks live in
+// one of two stores, kept per thread and reused, whose entries are all
+// zero between plans (a plan clears what it set):
+//   - dense: one mark per pool block, when the pool has at most four
+//     blocks per table entry the step covers;
+//   - hashed: an open-addressing table of 2-4 slots per table entry,
+//     otherwise.
+// Either way a plan costs time in proportion to the table entries it
+// covers, and the memory it walks stays within a small multiple of them,
+// however large the pool.
+struct BlockMarks {
+    std::vector<uint32_t> dense;
+    struct Slot {
+        int32_t id;      // -1: empty
+        uint32_t mark;
+    };
+    std::vector<Slot> hashed;
+    std::vector<uint32_t> used;   // hashed slots in use
+    uint32_t mask = 0;
+    int shift = 32;
+    bool is_dense = true;
+
+    void prepare(int32_t nb, int64_t entries) {
+        is_dense = (int64_t)nb <= 4 * entries;
+        if (is_dense) {
+            if ((int64_t)dense.size() < nb) dense.assign((size_t)nb, 0u);
+            return;
+        }
+        size_t cap = 64;
+        int bits = 6;
+        while ((int64_t)cap < 2 * entries) {
+            cap <<= 1;
+            ++bits;
+        }
+        if (hashed.size() < cap) hashed.assign(cap, Slot{-1, 0u});
+        mask = (uint32_t)(cap - 1);
+        shift = 32 - bits;
+        used.clear();
+        used.reserve((size_t)entries);
+    }
+    // start fetching the mark of id (the loop over table entries issues
+    // these a few entries ahead, so that the random accesses overlap)
+    void prefetch(int32_t id) const {
+        if (is_dense) __builtin_prefetch(dense.data() + id, 1);
+        else __builtin_prefetch(hashed.data() + (((uint32_t)id * 0x9E3779B1u) >> shift), 1);
+    }
+    uint32_t &at(int32_t id) {
+        if (is_dense) return dense[(size_t)id];
+        uint32_t h = ((uint32_t)id * 0x9E3779B1u) >> shift;
+        while (hashed[h].id != id && hashed[h].id != -1) h = (h + 1) & mask;
+        if (hashed[h].id == -1) {
+            hashed[h].id = id;
+            used.push_back(h);
+        }
+        return hashed[h].mark;
+    }
+    // zero every mark a plan over `entries` table entries set
+    template <class ForEachId>
+    void clear(int32_t nb, int64_t entries, ForEachId each_id) {
+        if (!is_dense) {
+            for (uint32_t h : used) hashed[h] = Slot{-1, 0u};
+            used.clear();
+        } else if ((int64_t)nb <= 8 * entries) {
+            std::memset(dense.data(), 0, sizeof(uint32_t) * (size_t)nb);
+        } else {
+            each_id([&](int32_t id) { dense[(size_t)id] = 0u; });
+        }
+    }
+};
+
+thread_local BlockMarks t_marks;
+
+bool is_multiple_in(int64_t v, int64_t m, int64_t lo, int64_t hi) { return v % m == 0 && v >= lo && v <= hi; }
+
+ps_status check_options(const ps_plan_options &o, uint32_t flags, const ps_pool *pool, int32_t g) {
+    if (o.decode_split_keys && !is_multiple_in(o.decode_split_keys, PS_BLOCK, PS_BLOCK, PS_DEC_MAX_SPLIT))
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "decode_split_keys %d: a multiple of 16 in [16, %d]",
+                       o.decode_split_keys, PS_DEC_MAX_SPLIT);
+    if (o.prefill_split_keys && !is_multiple_in(o.prefill_split_keys, PS_PRE_TILE, PS_PRE_TILE, PS_PRE_MAX_KEYS))
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "prefill_split_keys %d: a multiple of 64 in [64, %d]",
+                       o.prefill_split_keys, PS_PRE_MAX_KEYS);
+    if (o.prefix_slice_keys && !is_multiple_in(o.prefix_slice_keys, PS_PRE_TILE, PS_PRE_TILE, PS_PRE_MAX_KEYS))
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "prefix_slice_keys %d: a multiple of 64 in [64, %d]",
+                       o.prefix_slice_keys, PS_PRE_MAX_KEYS);
+    if (o.decode_waves != 0 && o.decode_waves != 4 && o.decode_waves != 8 && o.decode_waves != 16)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "decode_waves %d: 0, 4, 8 or 16", o.decode_waves);
+    if (o.decode_waves == 16 && (pool->head_dim != 64 || pool->dtype == PS_F32))
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "decode_waves 16 needs head_dim 64 and 16-bit data");
+    if (o.prefix_min_seqs < 0 || o.prefix_min_seqs == 1 || o.prefix_min_keys < 0 ||
+        (o.prefix_min_keys > 0 && o.prefix_min_keys < PS_BLOCK))
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "prefix_min_seqs must be 0 or >= 2, prefix_min_keys 0 or >= 16");
+    for (int i = 0; i < 4; ++i)
+        if (o.reserved[i] != 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "reserved option fields must be 0");
+    if (flags & PS_PLAN_FIXED_SHAPE) {
+        if ((flags & 3) == PS_PLAN_ALL_PREFILL || (flags & PS_PLAN_SHARED_PREFIX))
+            return ps_fail(PS_ERR_INVALID_ARGUMENT,
+                           "PS_PLAN_FIXED_SHAPE runs every sequence on the decode kernel: no "
+                           "PS_PLAN_ALL_PREFILL, no PS_PLAN_SHARED_PREFIX");
+        if (o.max_seqs < 1 || o.max_tokens < 1 || o.max_query_len < 1 || o.max_decode_items < 0 ||
+            o.max_merge_items < 0 || o.max_workspace_rows < 0)
+            return ps_fail(PS_ERR_INVALID_ARGUMENT, "fixed shape needs max_seqs, max_tokens, max_query_len >= 1");
+        if ((int64_t)g * o.max_query_len > PS_DEC_MAX_ROWS)
+            return ps_fail(PS_ERR_INVALID_ARGUMENT,
+                           "fixed shape: %d query heads per KV head x max_query_len %d exceeds %d rows", g,
+                           o.max_query_len, PS_DEC_MAX_ROWS);
+        if ((o.max_decode_items == 0 ? (int64_t)o.max_seqs * pool->num_kv_heads : o.max_decode_items) > INT32_MAX / 2)
+            return ps_fail(PS_ERR_INVALID_ARGUMENT, "fixed shape capacity too large");
+    }
+    return PS_OK;
+}
+
 }  // namespace
 
 extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_computed_tokens,
                                   int32_t num_seqs, const int32_t *block_tables,
                                   int32_t block_table_stride, int32_t num_q_heads,
-                                  const ps_pool *pool, uint32_t flags, ps_plan **out_plan) {
+                                  const ps_pool *pool, uint32_t flags, const ps_plan_options *options,
+                                  ps_plan **out_plan) {
+    const auto t_start = std::chrono::steady_clock::now();
     if (!out_plan) return ps_fail(PS_ERR_INVALID_ARGUMENT, "out_plan is NULL");
     *out_plan = nullptr;
     if (!pool) return ps_fail(PS_ERR_INVALID_ARGUMENT, "pool is NULL");
     if (num_seqs < 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_seqs < 0");
     if (num_seqs > 0 && (!q_lens || !num_computed_tokens || !block_tables))
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "q_lens, num_computed_tokens and block_tables must be non-NULL");
-    if (flags > PS_PLAN_ALL_PREFILL) return ps_fail(PS_ERR_INVALID_ARGUMENT, "unknown plan flags %u", flags);
+    const uint32_t known = 3u | PS_PLAN_SHARED_PREFIX | PS_PLAN_SEPARATE_LAUNCHES | PS_PLAN_FIXED_SHAPE;
+    if ((flags & ~known) != 0 || (flags & 3) == 3)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "unknown plan flags %u", flags);
     if (pool->block_size != PS_BLOCK)
         return ps_fail(PS_ERR_UNSUPPORTED, "block_size %d (only 16 is supported)", pool->block_size);
     if (pool->head_dim != 64 && pool->head_dim != 128)
@@ -102,15 +213,22 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
     if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads != 0)
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
                        num_q_heads, pool->num_kv_heads);
-    if (num_seqs > 0 && block_table_stride < 1)
+    if ((num_seqs > 0 || (flags & PS_PLAN_FIXED_SHAPE)) && block_table_stride < 1)
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "block_table_stride %d < 1", block_table_stride);
 
     const int32_t S = num_seqs;
     const int32_t Hkv = pool->num_kv_heads, D = pool->head_dim, NB = pool->num_blocks;
     const int32_t g = num_q_heads / Hkv;
+    const uint32_t route = flags & 3;
+    const bool fixed = (flags & PS_PLAN_FIXED_SHAPE) != 0;
+    const ps_plan_options opt = options ? *options : ps_plan_options{};
+    {
+        const ps_status st = check_options(opt, flags, pool, g);
+        if (st != PS_OK) return st;
+    }
 
     // ---- per-sequence checks
-    int64_t T = 0;
+    int64_t T = 0, n_entries = 0;
     for (int32_t s = 0; s < S; ++s) {
         const int64_t n = q_lens[s], c = num_computed_tokens[s];
         if (n < 1) return ps_fail(PS_ERR_INVALID_ARGUMENT, "q_lens[%d] = %lld < 1", s, (long long)n);
@@ -122,40 +240,84 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                            (long long)ctx, (long long)ceil_div(ctx, PS_BLOCK), block_table_stride);
         if ((int64_t)g * n > INT32_MAX / 2 || ctx > INT32_MAX / 2)
             return ps_fail(PS_ERR_UNSUPPORTED, "sequence %d too long", s);
+        if (fixed && n > opt.max_query_len)
+            return ps_fail(PS_ERR_INVALID_ARGUMENT, "q_lens[%d] = %lld exceeds the fixed shape's max_query_len %d",
+                           s, (long long)n, opt.max_query_len);
         T += n;
+        n_entries += ceil_div(ctx, PS_BLOCK);
     }
     if (T > INT32_MAX / 2) return ps_fail(PS_ERR_UNSUPPORTED, "too many tokens (%lld)", (long long)T);
+    if (fixed && (S > opt.max_seqs || T > opt.max_tokens))
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "step of %d sequences / %lld tokens exceeds the fixed shape's %d / %d",
+                       S, (long long)T, opt.max_seqs, opt.max_tokens);
 
-    // ---- block ids, duplicates within a table, shared blocks
-    std::vector<int32_t> refs, seen;
+    // ---- block ids, duplicates within a table, shared blocks: one pass
+    // over the table entries the step covers
+    if (S >= (1 << 25)) return ps_fail(PS_ERR_UNSUPPORTED, "too many sequences (%d)", S);
+    BlockMarks &bm = t_marks;
     try {
-        refs.assign(NB, 0);
-        seen.assign(NB, -1);
+        bm.prepare(NB, n_entries);
     } catch (const std::bad_alloc &) {
         return ps_fail(PS_ERR_HOST_MEMORY, "host allocation failed");
     }
-    for (int32_t s = 0; s < S; ++s) {
-        const int32_t *row = block_tables + (int64_t)s * block_table_stride;
-        const int64_t nblk = ceil_div((int64_t)num_computed_tokens[s] + q_lens[s], PS_BLOCK);
-        for (int64_t b = 0; b < nblk; ++b) {
-            const int32_t id = row[b];
-            if (id < 0 || id >= NB)
-                return ps_fail(PS_ERR_INVALID_ARGUMENT, "block_tables[%d][%lld] = %d outside [0, %d)", s,
-                               (long long)b, id, NB);
-            if (seen[id] == s)
-                return ps_fail(PS_ERR_INVALID_ARGUMENT, "block %d appears twice in the table of sequence %d", id, s);
-            seen[id] = s;
-            refs[id] += 1;
+    int64_t kv_rows_unique = 0;   // distinct (physical block, token) rows the step reads
+    {
+        // clears every mark the step's entries may have set (also after an
+        // error part way through)
+        struct Clear {
+            BlockMarks &bm;
+            const int32_t *q_lens, *nc, *bt;
+            int32_t S, stride, NB;
+            int64_t entries;
+            ~Clear() {
+                bm.clear(NB, entries, [&](auto zero) {
+                    for (int32_t s = 0; s < S; ++s) {
+                        const int32_t *row = bt + (int64_t)s * stride;
+                        const int64_t nblk = ceil_div((int64_t)nc[s] + q_lens[s], PS_BLOCK);
+                        for (int64_t b = 0; b < nblk; ++b)
+                            if (row[b] >= 0 && row[b] < NB) zero(row[b]);
+                    }
+                });
+            }
+        } clear{bm, q_lens, num_computed_tokens, block_tables, S, block_table_stride, NB, n_entries};
+        constexpr uint32_t kShared = 1u << 5;
+        for (int32_t s = 0; s < S; ++s) {
+            const int32_t *row = block_tables + (int64_t)s * block_table_stride;
+            const int64_t ctx = (int64_t)num_computed_tokens[s] + q_lens[s];
+            const int64_t nblk = ceil_div(ctx, PS_BLOCK);
+            const uint32_t tag = (uint32_t)(s + 1) << 6;
+            constexpr int64_t kAhead = 16;
+            for (int64_t b = 0; b < std::min(nblk, kAhead); ++b)
+                if (row[b] >= 0 && row[b] < NB) bm.prefetch(row[b]);
+            for (int64_t b = 0; b < nblk; ++b) {
+                const int32_t id = row[b];
+                if (id < 0 || id >= NB)
+                    return ps_fail(PS_ERR_INVALID_ARGUMENT, "block_tables[%d][%lld] = %d outside [0, %d)", s,
+                                   (long long)b, id, NB);
+                if (b + kAhead < nblk && row[b + kAhead] >= 0 && row[b + kAhead] < NB) bm.prefetch(row[b + kAhead]);
+                const uint32_t ntok = (uint32_t)std::min<int64_t>(PS_BLOCK, ctx - b * PS_BLOCK);
+                uint32_t &m = bm.at(id);
+                if (m == 0u) {
+                    m = tag | ntok;
+                    kv_rows_unique += ntok;
+                } else {
+                    if ((m >> 6) == (uint32_t)(s + 1))
+                        return ps_fail(PS_ERR_INVALID_ARGUMENT, "block %d appears twice in the table of sequence %d",
+                                       id, s);
+                    const uint32_t old = m & 31u;
+                    kv_rows_unique += ntok > old ? ntok - old : 0;
+                    m = tag | kShared | std::max(ntok, old);
+                }
+            }
         }
-    }
-    for (int32_t s = 0; s < S; ++s) {
-        const int32_t *row = block_tables + (int64_t)s * block_table_stride;
-        const int64_t c = num_computed_tokens[s], ctx = c + q_lens[s];
-        for (int64_t b = c / PS_BLOCK; b < ceil_div(ctx, PS_BLOCK); ++b) {
-            if (refs[row[b]] > 1)
-                return ps_fail(PS_ERR_INVALID_ARGUMENT,
-                               "sequence %d writes new tokens into block %d, which %d tables share "
-                               "(copy it before writing)", s, row[b], refs[row[b]]);
+        for (int32_t s = 0; s < S; ++s) {
+            const int32_t *row = block_tables + (int64_t)s * block_table_stride;
+            const int64_t c = num_computed_tokens[s], ctx = c + q_lens[s];
+            for (int64_t b = c / PS_BLOCK; b < ceil_div(ctx, PS_BLOCK); ++b)
+                if (bm.at(row[b]) & kShared)
+                    return ps_fail(PS_ERR_INVALID_ARGUMENT,
+                                   "sequence %d writes new tokens into block %d, which other tables share "
+                                   "(copy it before writing)", s, row[b]);
         }
     }
 
@@ -169,8 +331,9 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
     p->dtype = pool->dtype;
     p->num_blocks = NB;
     p->num_layers = pool->num_layers;
-    p->bt_stride = S > 0 ? block_table_stride : 1;
+    p->bt_stride = S > 0 || fixed ? std::max(1, block_table_stride) : 1;
     p->flags = flags;
+    p->fixed = fixed;
 
     try {
         // ---- work lists
@@ -179,29 +342,30 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         std::vector<char> is_dec(S);
         for (int32_t s = 0; s < S; ++s) {
             const int64_t rows = (int64_t)g * q_lens[s];
-            is_dec[s] = (flags == PS_PLAN_ALL_DECODE) ||
-                        (flags == PS_PLAN_DEFAULT && rows <= PS_DEC_MAX_ROWS);
+            is_dec[s] = (route == PS_PLAN_ALL_DECODE) || fixed ||
+                        (route == PS_PLAN_DEFAULT && rows <= PS_DEC_MAX_ROWS);
         }
-        const int64_t pre_rows = ps_prefill_rows(pool->dtype);
+        const int64_t pre_rows = PS_PRE_ROWS;
+        const bool mixed_ok = !(flags & PS_PLAN_SEPARATE_LAUNCHES) && pool->dtype != PS_F32;
 
-        // ---- shared prefixes. Decode sequences whose tables open with the
-        // same physical blocks (blocks shared by reference, PageServe "03
-        // Paged KV cache") form a group. Attention over the shared prefix
-        // then runs once per group, in prefill-kernel items whose query
-        // rows are gathered from every member: each prefix key lies below
-        // every member's first query position, so no mask applies. Each
-        // member's decode items cover only its keys after the prefix, and
-        // the partial softmax states merge like key splits. A member must
-        // share at least PS_CASCADE_MIN_KEYS tokens (whole blocks of its
-        // cached context) with the group's first sequence, and a group
-        // needs PS_CASCADE_MIN_SEQS members; PS_CASCADE=0 turns it off.
+        // ---- shared prefixes (PS_PLAN_SHARED_PREFIX). Decode sequences
+        // whose tables open with the same physical blocks (blocks shared by
+        // reference, PageServe "03 Paged KV cache") form a group. Attention
+        // over the shared prefix then runs once per group, in prefill-kernel
+        // items whose query rows are gathered from every member: each prefix
+        // key lies below every member's first query position, so no mask
+        // applies. Each member's decode items cover only its keys after the
+        // prefix, and the partial softmax states merge like key splits. A
+        // member must share at least prefix_min_keys tokens (whole blocks of
+        // its cached context) with the group's first sequence, and a group
+        // needs prefix_min_seqs members.
         std::vector<int32_t> grp_of(S, -1);
         std::vector<int32_t> grp_lead;
         std::vector<int64_t> grp_keys;
         std::vector<std::vector<int64_t>> grp_bounds;
-        if (flags == PS_PLAN_DEFAULT && env_on("PS_CASCADE", true)) {
-            const int64_t min_seqs = std::max<int64_t>(2, env_int("PS_CASCADE_MIN_SEQS", 8));
-            const int64_t min_blocks = ceil_div(std::max<int64_t>(16, env_int("PS_CASCADE_MIN_KEYS", 256)), PS_BLOCK);
+        if ((flags & PS_PLAN_SHARED_PREFIX) && route == PS_PLAN_DEFAULT) {
+            const int64_t min_seqs = opt.prefix_min_seqs ? opt.prefix_min_seqs : 8;
+            const int64_t min_blocks = ceil_div(opt.prefix_min_keys ? opt.prefix_min_keys : 256, PS_BLOCK);
             // candidates, sorted by their first min_blocks block ids: runs of
             // equal keys are the groups
             std::vector<int32_t> cand;
@@ -241,22 +405,25 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                 a0 = a1;
             }
             // prefix slices: about 128 prefix items per step (they share the
-            // launch with the decode items), none shorter than 256 keys
+            // launch with the decode items), none shorter than 256 keys and
+            // none longer than a prefill item's staged block list
             grp_bounds.resize(grp_lead.size());
+            std::vector<int64_t> grp_rows(grp_lead.size(), 0);
+            for (int32_t s = 0; s < S; ++s)
+                if (grp_of[s] >= 0) grp_rows[grp_of[s]] += (int64_t)g * q_lens[s];
             for (size_t gi = 0; gi < grp_lead.size(); ++gi) {
-                int64_t rows = 0;
-                for (int32_t s = 0; s < S; ++s)
-                    if (grp_of[s] == (int32_t)gi) rows += (int64_t)g * q_lens[s];
-                const int64_t chunks = ceil_div(rows, pre_rows) * Hkv;
+                const int64_t chunks = ceil_div(grp_rows[gi], pre_rows) * Hkv;
                 const int64_t want = std::max<int64_t>(1, std::min<int64_t>(ceil_div(128, chunks), grp_keys[gi] / 256));
-                const int64_t slice = env_int("PS_CASCADE_SLICE_KEYS", round_up(ceil_div(grp_keys[gi], want), PS_PRE_TILE));
-                key_splits(grp_keys[gi], std::max<int64_t>(PS_BLOCK, slice), PS_PRE_TILE, grp_bounds[gi]);
+                const int64_t slice = opt.prefix_slice_keys ? opt.prefix_slice_keys
+                                                            : round_up(ceil_div(grp_keys[gi], want), PS_PRE_TILE);
+                key_splits(grp_keys[gi], std::min<int64_t>(slice, PS_PRE_MAX_KEYS), PS_PRE_TILE, grp_bounds[gi]);
             }
         }
         // decode: a work item covers <= 32 packed rows and a slice of keys.
         // Slices are long (>= 2048 keys): a split costs a merge launch and
         // partial traffic, which only pays off against long contexts; very
-        // long steps are cut into about 512 items (two per CU).
+        // long steps are cut into about 512 items (two per CU). A fixed
+        // shape does not split unless told to.
         int64_t dec_keys = 0, pre_kmax = 0, pre_tiles = 0;
         for (int32_t s = 0; s < S; ++s) {
             const int64_t rows = (int64_t)g * q_lens[s], c = num_computed_tokens[s];
@@ -269,11 +436,11 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                 else { pre_kmax = std::max(pre_kmax, kmax); pre_tiles += Hkv; }
             }
         }
-        const int64_t dec_split = std::min<int64_t>(
-            PS_DEC_MAX_SPLIT,
-            round_up(std::max<int64_t>(PS_BLOCK, env_int("PS_DECODE_SPLIT",
-                                                         std::max<int64_t>(2048, round_up(ceil_div(dec_keys, 512), 128)))),
-                     PS_BLOCK));
+        const int64_t dec_split =
+            opt.decode_split_keys ? opt.decode_split_keys
+            : fixed               ? PS_DEC_MAX_SPLIT
+                                  : std::min<int64_t>(PS_DEC_MAX_SPLIT,
+                                                      std::max<int64_t>(2048, round_up(ceil_div(dec_keys, 512), 128)));
         // Prefill: aim for three full rounds of resident workgroups (256 CUs
         // x 2 = 512): each (row block, KV head) gets at most 1536 / blocks
         // slices, sized from the longest key range so that no block gets
@@ -281,7 +448,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         // than ~512 keys costs more in partials (a 128-row tile's partials
         // weigh as much as ~500 keys of K/V) than it balances.
         const int64_t pre_slices = std::max<int64_t>(1, 1536 / std::max<int64_t>(1, pre_tiles));
-        int64_t pre_auto = pre_tiles >= 512 ? INT32_MAX
+        int64_t pre_auto = pre_tiles >= 512 ? PS_PRE_MAX_KEYS
                                             : std::max<int64_t>(512, round_up(ceil_div(pre_kmax, pre_slices), PS_PRE_TILE));
         // In a mixed launch the decode items keep the chip busy while the
         // prefill items run. Slicing then pays only if an unsliced prefill
@@ -289,20 +456,20 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         // launch and the partials. Time models measured on MI355X: a
         // 128-row prefill item at ~1.9 TFLOP/s (two per CU), decode K/V
         // reads at ~4 TB/s.
-        if (dec_keys > 0 && ps_mixed_launch(pool->dtype)) {
+        if (dec_keys > 0 && mixed_ok) {
             const double t_dec = (double)dec_keys * 2.0 * D * elt_bytes(pool->dtype) / 4.0e6;  // us
             const double t_pre = (double)pre_kmax * pre_rows * 4.0 * D / 1.9e6;               // us
-            if (t_pre <= 2.0 * t_dec) pre_auto = INT32_MAX;
+            if (t_pre <= 2.0 * t_dec) pre_auto = PS_PRE_MAX_KEYS;
         }
-        const int64_t pre_split = env_int("PS_PREFILL_SPLIT", pre_auto);
+        const int64_t pre_split = std::min<int64_t>(
+            PS_PRE_MAX_KEYS, opt.prefill_split_keys ? opt.prefill_split_keys : round_up(pre_auto, PS_PRE_TILE));
 
         std::vector<int64_t> bounds;
         int64_t ws_rows = 0;
         int32_t dec_rt = 1;
-        int32_t qs_run = 0;   // query_start_loc[s]
         // gathered rows of each (group, KV head): the prefix items' row maps
         std::vector<std::vector<ps_row>> grows(grp_lead.size() * (size_t)Hkv);
-        for (int32_t s = 0; s < S; qs_run += q_lens[s], ++s) {
+        for (int32_t s = 0; s < S; ++s) {
             const int64_t rows = (int64_t)g * q_lens[s], c = num_computed_tokens[s];
             const bool d = is_dec[s];
             const int64_t rb = d ? PS_DEC_MAX_ROWS : pre_rows;
@@ -313,8 +480,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                 for (int64_t r0 = 0; r0 < rows; r0 += rb) {
                     const int64_t r1 = std::min(rows, r0 + rb);
                     const int64_t kmax = c + (r1 - 1) / g + 1;
-                    key_splits(kmax - pk, d ? dec_split : std::min<int64_t>(pre_split, PS_PRE_MAX_KEYS),
-                               d ? PS_BLOCK : PS_PRE_TILE, bounds);
+                    key_splits(kmax - pk, d ? dec_split : pre_split, d ? PS_BLOCK : PS_PRE_TILE, bounds);
                     for (int64_t &b : bounds) b += pk;
                     const int64_t ns = (int64_t)bounds.size() - 1;
                     const int64_t nsplit = npk + ns;   // partial sets the merge combines
@@ -325,7 +491,8 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                         std::vector<ps_row> &gr = grows[(size_t)gi * Hkv + j];
                         for (int64_t r = r0; r < r1; ++r) {
                             ps_row e{};
-                            e.q_row = (int32_t)((qs_run + r / g) * num_q_heads + j * g + r % g);
+                            e.seq = s;
+                            e.row = (int32_t)r;
                             e.dest = (int32_t)(base + (r - r0));
                             e.stride = (int32_t)(r1 - r0);
                             gr.push_back(e);
@@ -341,8 +508,6 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                         it.key_end = (int32_t)bounds[i + 1];
                         it.partial_row = nsplit > 1 ? (int32_t)(base + (npk + i) * (r1 - r0)) : -1;
                         it.flags = r1 == rows && i == ns - 1 ? PS_ITEM_WRITES_NEW : 0;
-                        it.q_start = qs_run;
-                        it.num_computed = (int32_t)c;
                         if (d) {
                             const int64_t ntiles = ceil_div(it.key_end - it.key_begin, PS_DEC_TILE);
                             it.rot = ntiles > 1 ? (int32_t)((dec.size() * 13) % (size_t)ntiles) : 0;
@@ -360,7 +525,6 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                             m.partial_row = (int32_t)(base + (q0 - r0));
                             m.num_splits = (int32_t)nsplit;
                             m.split_stride = (int32_t)(r1 - r0);
-                            m.q_start = qs_run;
                             mrg.push_back(m);
                         }
                         ws_rows += nsplit * (r1 - r0);
@@ -399,6 +563,19 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
             delete p;
             return ps_fail(PS_ERR_UNSUPPORTED, "split-K workspace too large");
         }
+        // Every item's key span fits the block ids its kernel stages in LDS.
+        for (const ps_item &it : dec)
+            if (it.key_end - it.key_begin > PS_DEC_MAX_SPLIT || it.key_end <= it.key_begin) {
+                delete p;
+                return ps_fail(PS_ERR_UNSUPPORTED, "decode item of %d keys (internal limit %d)",
+                               it.key_end - it.key_begin, PS_DEC_MAX_SPLIT);
+            }
+        for (const ps_item &it : pre)
+            if (it.key_end - it.key_begin > PS_PRE_MAX_KEYS || it.key_end <= it.key_begin) {
+                delete p;
+                return ps_fail(PS_ERR_UNSUPPORTED, "prefill item of %d keys (internal limit %d)",
+                               it.key_end - it.key_begin, PS_PRE_MAX_KEYS);
+            }
         // Longest decode items first (longest-processing-time order): in a
         // launch with more items than resident workgroups the ones that
         // start late are the short ones, and in a mixed launch the longest
@@ -411,12 +588,45 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
             std::stable_sort(dec.begin(), dec.end(), [](const ps_item &x, const ps_item &y) {
                 return x.key_end - x.key_begin > y.key_end - y.key_begin;
             });
+
+        // ---- launch shape (fixed: from the capacities alone)
+        const int32_t act_dec = (int32_t)dec.size(), act_mrg = (int32_t)mrg.size();
+        int64_t cap_dec = act_dec, cap_mrg = act_mrg, cap_ws = ws_rows;
+        int64_t cap_S = S, cap_T = T;
+        if (fixed) {
+            cap_dec = opt.max_decode_items ? opt.max_decode_items : (int64_t)opt.max_seqs * Hkv;
+            cap_mrg = opt.max_merge_items;
+            cap_ws = opt.max_workspace_rows;
+            cap_S = opt.max_seqs;
+            cap_T = opt.max_tokens;
+            if (act_dec > cap_dec || act_mrg > cap_mrg || ws_rows > cap_ws) {
+                delete p;
+                return ps_fail(PS_ERR_INVALID_ARGUMENT,
+                               "step needs %d decode items, %d merges, %lld partial rows; the fixed shape "
+                               "holds %lld, %lld, %lld", act_dec, act_mrg, (long long)ws_rows,
+                               (long long)cap_dec, (long long)cap_mrg, (long long)cap_ws);
+            }
+            dec_rt = (int32_t)ceil_div((int64_t)g * opt.max_query_len, 16);
+            ps_item idle{};
+            idle.seq = -1;
+            dec.resize((size_t)cap_dec, idle);
+            ps_merge midle{};
+            midle.seq = -1;
+            mrg.resize((size_t)cap_mrg, midle);
+        }
         p->dec_rt = dec_rt;
-        p->ws_rows = ws_rows;
+        p->ws_rows = cap_ws;
+        p->rows_cap = (int32_t)cap_T;
         p->n_dec = (int32_t)dec.size();
         p->n_pre = (int32_t)pre.size();
         p->n_mrg = (int32_t)mrg.size();
         p->n_gathered = n_gathered;
+        p->mixed = mixed_ok && p->n_dec > 0 && p->n_pre > 0;
+        // few decode items: more waves per item, so a short slice is read in
+        // one round trip; many items: 4 waves each fill the chip
+        p->dec_waves = opt.decode_waves ? opt.decode_waves : (p->n_dec < 512 ? 8 : 4);
+        if (dec_rt == 2 || p->mixed || p->dtype == PS_F32 || D != 64) p->dec_waves = std::min(p->dec_waves, 8);
+        if (dec_rt == 2 || p->mixed) p->dec_waves = 4;
 
         // ---- blob layout
         size_t off = 0;
@@ -425,12 +635,12 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
             off = ps_align256(off + std::max<size_t>(bytes, 1));
             return o;
         };
-        p->off_qsl = take(sizeof(int32_t) * (S + 1));
-        p->off_nc = take(sizeof(int32_t) * S);
-        p->off_ctx = take(sizeof(int32_t) * S);
-        p->off_slot = take(sizeof(int32_t) * (size_t)T);
-        p->off_pos = take(sizeof(int32_t) * (size_t)T);
-        p->off_bt = take(sizeof(int32_t) * (size_t)S * p->bt_stride);
+        p->off_qsl = take(sizeof(int32_t) * (size_t)(cap_S + 1));
+        p->off_nc = take(sizeof(int32_t) * (size_t)cap_S);
+        p->off_ctx = take(sizeof(int32_t) * (size_t)cap_S);
+        p->off_slot = take(sizeof(int32_t) * (size_t)cap_T);
+        p->off_pos = take(sizeof(int32_t) * (size_t)cap_T);
+        p->off_bt = take(sizeof(int32_t) * (size_t)cap_S * p->bt_stride);
         p->off_dec = take(sizeof(ps_item) * dec.size());
         p->off_pre = take(sizeof(ps_item) * pre.size());
         p->off_mrg = take(sizeof(ps_merge) * mrg.size());
@@ -457,6 +667,8 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                 posn[qsl[s] + i] = (int32_t)pos;
             }
         }
+        for (int64_t s = S; s < cap_S; ++s) qsl[s + 1] = (int32_t)T;   // fixed shape: unused tail
+        for (int64_t t = T; t < cap_T; ++t) slot[t] = -1;               // (skipped by any scatter)
         if (!dec.empty()) std::memcpy(p->host<ps_item>(p->off_dec), dec.data(), sizeof(ps_item) * dec.size());
         if (!pre.empty()) std::memcpy(p->host<ps_item>(p->off_pre), pre.data(), sizeof(ps_item) * pre.size());
         if (!mrg.empty()) std::memcpy(p->host<ps_merge>(p->off_mrg), mrg.data(), sizeof(ps_merge) * mrg.size());
@@ -465,19 +677,23 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         // key_begin + 32 u .. +32, u = (t + rot) mod ntiles; a tile's second
         // block past key_end repeats the first (never read)
         int32_t *dh = p->host<int32_t>(p->off_dhead);
-        for (size_t i = 0; i < dec.size(); ++i) {
+        for (size_t i = 0; i < (size_t)act_dec; ++i) {
             const ps_item &it = dec[i];
             const int32_t *row = block_tables + (int64_t)it.seq * block_table_stride;
-            const int64_t ntiles = ceil_div(it.key_end - it.key_begin, PS_DEC_TILE);
-            for (int64_t t = 0; t < std::min<int64_t>(ntiles, PS_DEC_HEAD_TILES); ++t) {
-                const int64_t u = (t + it.rot) % ntiles, k0 = it.key_begin + u * PS_DEC_TILE;
+            const int32_t ntiles = (it.key_end - it.key_begin + PS_DEC_TILE - 1) / PS_DEC_TILE;
+            int32_t u = it.rot;
+            for (int32_t t = 0; t < std::min<int32_t>(ntiles, PS_DEC_HEAD_TILES); ++t) {
+                const int32_t k0 = it.key_begin + u * PS_DEC_TILE;
                 const int32_t b0 = row[k0 / PS_BLOCK];
                 dh[i * 2 * PS_DEC_HEAD_TILES + 2 * t] = b0;
                 dh[i * 2 * PS_DEC_HEAD_TILES + 2 * t + 1] = k0 + PS_BLOCK < it.key_end ? row[k0 / PS_BLOCK + 1] : b0;
+                u = u + 1 == ntiles ? 0 : u + 1;
             }
         }
+        p->kinds.resize(S);
+        for (int32_t s = 0; s < S; ++s) p->kinds[s] = !is_dec[s] ? 1 : grp_of[s] >= 0 ? 2 : 0;
 
-        // ---- algorithmic accounting
+        // ---- algorithmic accounting and the planner's choices
         ps_plan_info &I = p->info;
         I.num_seqs = S;
         I.num_tokens = (int32_t)T;
@@ -492,6 +708,14 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         I.step_fused = p->n_pre == n_gathered && p->n_dec > 0;
         I.merge_items = p->n_mrg;
         I.decode_row_tiles = dec_rt;
+        I.flags = (int32_t)flags;
+        I.decode_split_keys = (int32_t)dec_split;
+        I.prefill_split_keys = (int32_t)pre_split;
+        I.decode_waves = p->dec_waves;
+        I.mixed_launch = p->mixed;
+        I.active_decode_items = act_dec;
+        I.active_merge_items = act_mrg;
+        I.workspace_rows = cap_ws;
         const int64_t e = elt_bytes(pool->dtype);
         const int64_t row_kv = 2 * (int64_t)D * e;  // K + V bytes of one (token, KV head)
         for (int32_t s = 0; s < S; ++s) {
@@ -503,14 +727,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
             I.table_bytes += 4 * ceil_div(ctx, PS_BLOCK);
         }
         // unique: each physical block once, with the most tokens any sharer reads
-        std::vector<int32_t> used(NB, 0);
-        for (int32_t s = 0; s < S; ++s) {
-            const int32_t *row = block_tables + (int64_t)s * block_table_stride;
-            const int64_t ctx = (int64_t)num_computed_tokens[s] + q_lens[s];
-            for (int64_t b = 0; b < ceil_div(ctx, PS_BLOCK); ++b)
-                used[row[b]] = std::max<int32_t>(used[row[b]], (int32_t)std::min<int64_t>(PS_BLOCK, ctx - b * PS_BLOCK));
-        }
-        for (int32_t b = 0; b < NB; ++b) I.kv_bytes_unique += (int64_t)used[b] * Hkv * row_kv;
+        I.kv_bytes_unique = kv_rows_unique * Hkv * row_kv;
         I.q_bytes = T * num_q_heads * D * e;
         I.out_bytes = I.q_bytes;
         I.scatter_bytes = 2 * (T * Hkv * D * e) * 2 + 4 * T;
@@ -518,6 +735,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         delete p;
         return ps_fail(PS_ERR_HOST_MEMORY, "host allocation failed");
     }
+    p->info.plan_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_start).count();
     *out_plan = p;
     return PS_OK;
 }
@@ -573,6 +791,14 @@ extern "C" ps_status ps_plan_get_info(const ps_plan *plan, ps_plan_info *info) {
     return PS_OK;
 }
 
+extern "C" ps_status ps_plan_sequence_kernels(const ps_plan *plan, int32_t *kinds, int32_t num_seqs) {
+    if (!plan) return ps_fail(PS_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (num_seqs != plan->S) return ps_fail(PS_ERR_INVALID_ARGUMENT, "num_seqs %d, plan has %d", num_seqs, plan->S);
+    if (num_seqs > 0 && !kinds) return ps_fail(PS_ERR_INVALID_ARGUMENT, "kinds is NULL");
+    if (num_seqs > 0) std::memcpy(kinds, plan->kinds.data(), sizeof(int32_t) * (size_t)num_seqs);
+    return PS_OK;
+}
+
 extern "C" void ps_plan_destroy(ps_plan *plan) { delete plan; }
 
 // ---------------------------------------------------------------------------
@@ -599,7 +825,7 @@ static ps_status prepare_attention(const void *q, const ps_pool *pool, const int
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "pool geometry differs from the plan's");
     if (pool->layer < 0 || pool->layer >= pool->num_layers)
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", pool->layer, pool->num_layers);
-    if (num_seqs > 0 && block_table_stride != plan->bt_stride)
+    if ((num_seqs > 0 || plan->fixed) && block_table_stride != plan->bt_stride)
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "block_table_stride %d differs from the plan's %d",
                        block_table_stride, plan->bt_stride);
     if (!(scale > 0.0f) || !(scale < 1e30f))
@@ -611,7 +837,7 @@ static ps_status prepare_attention(const void *q, const ps_pool *pool, const int
     if (wl.bytes > 0 && (!workspace || ((uintptr_t)workspace & 255)))
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "workspace is NULL or not 256-byte aligned");
     if (!plan->dev) return ps_fail(PS_ERR_INVALID_ARGUMENT, "plan has not been uploaded");
-    if (num_tokens == 0) {
+    if (num_tokens == 0 && !plan->fixed) {
         *empty = true;
         return PS_OK;
     }
@@ -632,7 +858,11 @@ static ps_status prepare_attention(const void *q, const ps_pool *pool, const int
     a.decode_items = reinterpret_cast<const ps_item *>(dev + plan->off_dec);
     a.prefill_items = reinterpret_cast<const ps_item *>(dev + plan->off_pre);
     a.merges = reinterpret_cast<const ps_merge *>(dev + plan->off_mrg);
+    // the items' first block ids are copies of the plan's table: usable only
+    // when the call reads that very table
+    const int32_t *plan_bt = reinterpret_cast<const int32_t *>(dev + plan->off_bt);
     a.decode_head = reinterpret_cast<const int32_t *>(dev + plan->off_dhead);
+    a.head_ok = block_tables == plan_bt;
     a.row_map = reinterpret_cast<const ps_row *>(dev + plan->off_rmap);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     a.ws_m = wl.bytes ? reinterpret_cast<float *>(ws + wl.off_m) : nullptr;
@@ -641,6 +871,9 @@ static ps_status prepare_attention(const void *q, const ps_pool *pool, const int
     a.layer_offset = (int64_t)pool->layer * pool->num_blocks * PS_BLOCK * pool->num_kv_heads * pool->head_dim;
     a.bt_stride = plan->bt_stride;
     a.num_blocks = plan->num_blocks;
+    // a fixed shape's launch must not depend on this step's token count:
+    // its q and out hold max_tokens rows
+    a.num_tokens = std::max(1, plan->fixed ? plan->rows_cap : num_tokens);
     a.num_q_heads = plan->Hq;
     a.num_kv_heads = plan->Hkv;
     a.head_dim = plan->D;
@@ -649,9 +882,8 @@ static ps_status prepare_attention(const void *q, const ps_pool *pool, const int
     a.n_prefill = plan->n_pre;
     a.n_merge = plan->n_mrg;
     a.decode_row_tiles = plan->dec_rt;
-    // few decode items: more waves per item, so a short slice is read in
-    // one round trip; many items: 4 waves each fill the chip
-    a.decode_waves = (int32_t)env_int("PS_DECODE_WAVES", plan->n_dec < 512 ? 8 : 4);
+    a.decode_waves = plan->dec_waves;
+    a.mixed = plan->mixed;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.g = plan->Hq / plan->Hkv;
     ps_group_divisor(a.g, &a.g_magic, &a.g_shift);

@@ -20,8 +20,10 @@
 // issues all of its loads up front, then computes up to two of the
 // tokens' (cos, sin) pairs into LDS while those loads are in flight, and
 // only then rotates and stores: one memory round trip per thread, with
-// the fp64 angle math hidden under it. q_out may alias q: a thread reads
-// and writes only its own chunks, reads first.
+// the fp64 angle math hidden under it. A token with more than 512 units
+// (e.g. 64 query heads of 128) takes a workgroup of its own, whose
+// threads finish the units past the first 512 one at a time. q_out may
+// alias q: a thread reads and writes only its own chunks, reads first.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -120,10 +122,29 @@ __global__ __launch_bounds__(256) void ps_rope_cache_kernel(const ps_rope_launch
         freq[i] = a.inv_freq[idx % HALF];
     }
 
-    // 2. every load of this thread's units
+    // 2. every load of this thread's first units
     const u32x4 *q = static_cast<const u32x4 *>(a.q);
     const u32x4 *k = static_cast<const u32x4 *>(a.k);
     const u32x4 *v = static_cast<const u32x4 *>(a.v);
+    // unit u of the workgroup: its source words, kind, destination word
+    // and first angle
+    auto describe = [&](int u, const u32x4 *&src, int &hi_off, int64_t &t, int &kind, int64_t &dst, int &cbase) {
+        const int tok = u / per_tok;
+        const int r = u - tok * per_tok;
+        t = t0 + tok;
+        const bool rot = r < rot_units;
+        const int head = r / HC;
+        const int c = r - head * HC;
+        const bool isq = head < Hq;
+        const int64_t qw = (t * Hq + head) * ROW_W + c;
+        const int64_t kw = (t * Hkv + (head - Hq)) * ROW_W + c;
+        const int64_t vw = t * v_words + (r - rot_units);
+        src = rot ? (isq ? q + qw : k + kw) : v + vw;
+        hi_off = rot ? HC : 0;
+        kind = rot ? (isq ? 1 : 2) : 3;
+        dst = rot ? (isq ? qw : (int64_t)(head - Hq) * ROW_W + c) : (int64_t)(r - rot_units);
+        cbase = tok * HALF + c * CH;
+    };
     u32x4 lo[kUnitsPerThread], hi[kUnitsPerThread];
     int32_t slot[kUnitsPerThread];
     int kind[kUnitsPerThread];      // 0 none, 1 q, 2 k, 3 v
@@ -132,24 +153,14 @@ __global__ __launch_bounds__(256) void ps_rope_cache_kernel(const ps_rope_launch
 #pragma unroll
     for (int i = 0; i < kUnitsPerThread; ++i) {
         const int u0 = threadIdx.x + 256 * i;
-        const int u = min(u0, n_units - 1);
-        const int tok = u / per_tok;
-        const int r = u - tok * per_tok;
-        const int64_t t = t0 + tok;
-        const bool rot = r < rot_units;
-        const int head = r / HC;
-        const int c = r - head * HC;
-        const bool isq = head < Hq;
-        const int64_t qw = (t * Hq + head) * ROW_W + c;
-        const int64_t kw = (t * Hkv + (head - Hq)) * ROW_W + c;
-        const int64_t vw = t * v_words + (r - rot_units);
-        const u32x4 *src = rot ? (isq ? q + qw : k + kw) : v + vw;
+        const u32x4 *src;
+        int hi_off;
+        int64_t t;
+        describe(min(u0, n_units - 1), src, hi_off, t, kind[i], dst[i], cbase[i]);
         slot[i] = a.slots[t];
         lo[i] = src[0];
-        hi[i] = src[rot ? HC : 0];
-        kind[i] = u0 >= n_units ? 0 : rot ? (isq ? 1 : 2) : 3;
-        dst[i] = rot ? (isq ? qw : (int64_t)(head - Hq) * ROW_W + c) : (int64_t)(r - rot_units);
-        cbase[i] = tok * HALF + c * CH;
+        hi[i] = src[hi_off];
+        kind[i] = u0 >= n_units ? 0 : kind[i];
     }
 
     // 3. cos / sin of this workgroup's angles (fp64), shared through LDS
@@ -169,26 +180,39 @@ __global__ __launch_bounds__(256) void ps_rope_cache_kernel(const ps_rope_launch
     u32x4 *pk = static_cast<u32x4 *>(a.pool_k);
     u32x4 *pv = static_cast<u32x4 *>(a.pool_v);
     const uint32_t num_slots = (uint32_t)a.num_slots;
-#pragma unroll
-    for (int i = 0; i < kUnitsPerThread; ++i) {
-        if (kind[i] == 0) continue;
-        if (kind[i] != 1 && (uint32_t)slot[i] >= num_slots) continue;
-        if (kind[i] == 3) {
-            pv[(int64_t)slot[i] * v_words + dst[i]] = lo[i];
-            continue;
+    auto finish = [&](int kd, int32_t sl, int64_t dw, int cb, u32x4 w_lo, u32x4 w_hi) {
+        if (kd == 0) return;
+        if (kd != 1 && (uint32_t)sl >= num_slots) return;
+        if (kd == 3) {
+            pv[(int64_t)sl * v_words + dw] = w_lo;
+            return;
         }
         float x1[CH], x2[CH], y1[CH], y2[CH];
-        unpack(lo[i], x1, DT{});
-        unpack(hi[i], x2, DT{});
+        unpack(w_lo, x1, DT{});
+        unpack(w_hi, x2, DT{});
 #pragma unroll
         for (int e = 0; e < CH; ++e) {
-            const float2 f = cs[cbase[i] + e];
+            const float2 f = cs[cb + e];
             y1[e] = x1[e] * f.x - x2[e] * f.y;
             y2[e] = x2[e] * f.x + x1[e] * f.y;
         }
-        u32x4 *o = kind[i] == 1 ? q_out + dst[i] : pk + (int64_t)slot[i] * v_words + dst[i];
+        u32x4 *o = kd == 1 ? q_out + dw : pk + (int64_t)sl * v_words + dw;
         o[0] = pack(y1, DT{});
         o[HC] = pack(y2, DT{});
+    };
+#pragma unroll
+    for (int i = 0; i < kUnitsPerThread; ++i) finish(kind[i], slot[i], dst[i], cbase[i], lo[i], hi[i]);
+
+    // 5. a token of more units than two per thread (many heads) is one
+    //    workgroup's alone; its remaining units go one by one
+    for (int u = threadIdx.x + 256 * kUnitsPerThread; u < n_units; u += 256) {
+        const u32x4 *src;
+        int hi_off, kd, cb;
+        int64_t t, dw;
+        describe(u, src, hi_off, t, kd, dw, cb);
+        const int32_t sl = a.slots[t];
+        const u32x4 w_lo = src[0], w_hi = src[hi_off];
+        finish(kd, sl, dw, cb, w_lo, w_hi);
     }
 }
 

@@ -13,11 +13,12 @@ from . import _binding as B
 
 class PackedStep:
     def __init__(self, q_lens, num_computed_tokens, block_tables, num_q_heads: int,
-                 pool: B.ps_pool, device, flags: int = B.PS_PLAN_DEFAULT, stream=None):
+                 pool: B.ps_pool, device, flags: int = B.PS_PLAN_DEFAULT, stream=None, options=None):
         self.num_seqs = len(q_lens)
         self.num_tokens = int(sum(int(x) for x in q_lens))
         self.num_q_heads = num_q_heads
-        self.plan = B.ps_plan_step(q_lens, num_computed_tokens, block_tables, num_q_heads, pool, flags)
+        self.plan = B.ps_plan_step(q_lens, num_computed_tokens, block_tables, num_q_heads, pool, flags,
+                                   options)
         self.meta_bytes, self.ws_bytes = B.ps_plan_sizes(self.plan)
         self.meta = torch.empty(self.meta_bytes, dtype=torch.uint8, device=device)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)

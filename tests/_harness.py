@@ -78,3 +78,14 @@ def sample_rows(step, n_random: int, seed: int = 0) -> np.ndarray:
     rng = np.random.default_rng(1000 + seed)
     sel[rng.integers(0, T, n_random), rng.integers(0, H, n_random)] = True
     return sel
+
+
+# Measured error margins of every output check in this process (tests
+# append; conftest writes them out at the end of the session).
+MARGINS = []
+
+
+def record_margin(name, dtype, rows, max_abs, tol, max_rel, rtol):
+    MARGINS.append({"case": name, "dtype": dtype, "rows": rows, "max_abs": max_abs, "tol": tol,
+                    "abs_margin": tol / max_abs if max_abs > 0 else None, "max_row_rel_l2": max_rel,
+                    "rtol": rtol, "rel_margin": rtol / max_rel if max_rel > 0 else None})

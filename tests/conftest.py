@@ -19,3 +19,18 @@ def _oracle_built():
     if not os.path.exists(obuild.LIB):
         obuild.build()
     yield
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # the parity checks' measured error margins, when asked for
+    path = os.environ.get("PS_PARITY_MARGINS")
+    if not path:
+        return
+    try:
+        from tests import _harness
+    except ImportError:
+        return
+    if _harness.MARGINS:
+        import json
+        with open(path, "w") as f:
+            json.dump(_harness.MARGINS, f, indent=1)

@@ -1,13 +1,13 @@
 """GPU parity of steps whose decode sequences share prefix blocks.
 
-Sequences whose tables open with the same blocks are grouped by the
-planner: attention over the shared prefix runs once per group, in
-prefill-kernel items whose query rows are gathered from every member, and
-merges with each member's own keys like a key split. These cases check the
-result against the oracle (which knows nothing of groups) with the
-grouping on and off, across dtypes and head dims, with verify rows, key
-splits on both sides, several row ranges per sequence, a prefill chunk in
-the step (mixed launch) and the fused scatter.
+With PS_PLAN_SHARED_PREFIX, sequences whose tables open with the same
+blocks are grouped by the planner: attention over the shared prefix runs
+once per group, in prefill-kernel items whose query rows are gathered from
+every member, and merges with each member's own keys like a key split.
+These cases check the result against the oracle (which knows nothing of
+groups) with the grouping on and off, across dtypes and head dims, with
+verify rows, key splits on both sides, several row ranges per sequence, a
+prefill chunk in the step (mixed launch) and the fused scatter.
 """
 import numpy as np
 import pytest
@@ -25,12 +25,16 @@ CASES = [  # dtype, Hq, Hkv, D
 ]
 
 
-def _info(st, flags=P.PS_PLAN_DEFAULT):
+SP = P.PS_PLAN_SHARED_PREFIX
+
+
+def _info(st, flags=SP, **options):
     pool = P.ps_pool(0, 0, st.num_layers, st.num_blocks, 16, st.num_kv_heads, st.head_dim,
                      {torch.float32: P.PS_F32, torch.float16: P.PS_F16, torch.bfloat16: P.PS_BF16}[st.dtype],
                      st.layer)
     return P.ps_plan_get_info(P.ps_plan_step(st.q_lens, st.num_computed, st.block_tables,
-                                             st.num_q_heads, pool, flags))
+                                             st.num_q_heads, pool, flags,
+                                             P.plan_options(**options) if options else None))
 
 
 @pytest.mark.parametrize("with_prefill", [False, True])
@@ -45,38 +49,36 @@ def test_prefix_groups_match_oracle(case, verify, with_prefill):
           f"prefix_items={info['prefix_items']} fused={info['step_fused']}")
     assert info["prefix_groups"] >= 1
     pools = H.host_pools(st)
-    out, gk, gv = run_on_gpu(st, pools=pools)
+    out, gk, gv = run_on_gpu(st, SP, pools=pools)
     check_pool(st, pools, gk, gv)
     check_out(st, out)
 
 
 @pytest.mark.parametrize("case", CASES[:3], ids=lambda c: "-".join(map(str, c)))
-def test_prefix_groups_with_many_splits(case, monkeypatch):
+def test_prefix_groups_with_many_splits(case):
     # short slices on both sides of the prefix boundary: several prefix
     # slices per group and several key splits after it, merged per row
     dt, hq, hkv, d = case
-    monkeypatch.setenv("PS_CASCADE_SLICE_KEYS", "64")
-    monkeypatch.setenv("PS_DECODE_SPLIT", "48")
+    opts = dict(prefix_slice_keys=64, decode_split_keys=48)
     st = workloads.prefix_groups_step(11 + d, dtype=dt, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
                                       verify=True)
-    info = _info(st)
+    info = _info(st, **opts)
     _note(f"{st.summary()} prefix_items={info['prefix_items']} merges={info['merge_items']}")
     assert info["prefix_items"] >= 2 * hkv * 5
     pools = H.host_pools(st)
-    out, gk, gv = run_on_gpu(st, pools=pools)
+    out, gk, gv = run_on_gpu(st, SP, pools=pools, **opts)
     check_pool(st, pools, gk, gv)
     check_out(st, out)
 
 
 @pytest.mark.parametrize("separate", [False, True])
-def test_prefix_groups_on_and_off_agree(separate, monkeypatch):
+def test_prefix_groups_on_and_off_agree(separate):
     st = workloads.prefix_groups_step(21)
     pools = H.host_pools(st)
-    out_on, gk, gv = run_on_gpu(st, pools=pools, separate=separate)
+    out_on, gk, gv = run_on_gpu(st, SP, pools=pools, separate=separate)
     check_pool(st, pools, gk, gv)
     e_on = check_out(st, out_on)
-    monkeypatch.setenv("PS_CASCADE", "0")
-    assert _info(st)["prefix_groups"] == 0
+    assert _info(st, P.PS_PLAN_DEFAULT)["prefix_groups"] == 0
     out_off, _, _ = run_on_gpu(st, pools=pools, separate=separate)
     e_off = check_out(st, out_off)
     diff = (out_on.to(torch.float64) - out_off.to(torch.float64)).abs().max().item()
@@ -91,6 +93,6 @@ def test_config4_groups_whole_batch():
     info = _info(st)
     assert info["prefix_groups"] == 1 and info["step_fused"] == 1 and info["prefix_items"] > 0
     pools = H.host_pools(st)
-    out, gk, gv = run_on_gpu(st, pools=pools)
+    out, gk, gv = run_on_gpu(st, SP, pools=pools)
     check_pool(st, pools, gk, gv)
     check_out(st, out)

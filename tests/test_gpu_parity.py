@@ -6,7 +6,11 @@ ps_paged_attention on cuda:0, then checks
   * the whole pool (every layer) bit-exact against the oracle's scatter;
   * the attention output against the oracle's fp64 result within the
     tolerance for the dtype: max-abs <= 1e-5 (fp32), 2e-3 (fp16),
-    1e-2 (bf16), plus a per-row relative L2 bound.
+    1e-2 (bf16), and per-row relative L2 error within the same figures
+    (the absolute bound alone is loose for long contexts, whose outputs
+    shrink like sqrt(e / context)).
+The measured margins of every check are kept (tests/_harness.MARGINS) and
+written out at the end of the session when PS_PARITY_MARGINS names a file.
 """
 import os
 
@@ -33,14 +37,16 @@ def _to_dev_pool(arr, dtype):
     return torch.from_numpy(arr).to(DEV).view(dtype)
 
 
-def run_on_gpu(st, flags=P.PS_PLAN_DEFAULT, pools=None, repeat=1, separate=False):
+def run_on_gpu(st, flags=P.PS_PLAN_DEFAULT, pools=None, repeat=1, separate=False, **options):
     """Run the step through the library (ps_step, or the two calls with
-    ``separate``); returns (out, pool_k, pool_v) on the host."""
+    ``separate``); returns (out, pool_k, pool_v) on the host. Keyword
+    arguments are plan options (ps_plan_options fields)."""
     pk, pv = pools if pools is not None else H.host_pools(st)
     gk = _to_dev_pool(pk, st.dtype)
     gv = _to_dev_pool(pv, st.dtype)
     pool = P.make_pool(gk, gv, st.layer)
-    step = P.PackedStep(st.q_lens, st.num_computed, st.block_tables, st.num_q_heads, pool, DEV, flags)
+    step = P.PackedStep(st.q_lens, st.num_computed, st.block_tables, st.num_q_heads, pool, DEV, flags,
+                        options=P.plan_options(**options) if options else None)
     q, k, v = st.q.to(DEV), st.k.to(DEV), st.v.to(DEV)
     out = torch.full_like(q, float("nan"))
     stream = torch.cuda.current_stream()
@@ -58,18 +64,22 @@ def check_pool(st, pools_before, gk, gv):
     assert np.array_equal(gv, ev), "V pool differs from the oracle's scatter"
 
 
-def check_out(st, out, row_sel=None, tol=None):
-    ref = H.oracle_out(st, row_sel=row_sel)
+def check_out(st, out, row_sel=None, tol=None, rtol=None, ref=None):
+    ref = H.oracle_out(st, row_sel=row_sel) if ref is None else ref
     got = out.to(torch.float64).numpy()
     if row_sel is not None:
         ref, got = ref[row_sel], got[row_sel]
     assert np.all(np.isfinite(got)), "non-finite output"
     err = np.abs(got - ref)
     tol = TOL[st.dtype] if tol is None else tol
+    rtol = RTOL[st.dtype] if rtol is None else rtol
     rel = np.linalg.norm(got - ref, axis=-1) / np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
-    _note(f"{st.name}: max_abs={err.max():.3e} (tol {tol:g}) max_row_rel_l2={rel.max():.3e}")
+    rows = int(np.prod(got.shape[:-1]))
+    _note(f"{st.name}: rows={rows} max_abs={err.max():.3e} (tol {tol:g}) "
+          f"max_row_rel_l2={rel.max():.3e} (rtol {rtol:g})")
+    H.record_margin(st.name, st.dtype_name, rows, float(err.max()), tol, float(rel.max()), rtol)
     assert err.max() <= tol
-    assert rel.max() <= RTOL[st.dtype] * 4
+    assert rel.max() <= rtol
     return err.max()
 
 
@@ -83,17 +93,18 @@ def test_config_parity_full(idx):
     check_out(st, out)
 
 
-def test_config5_parity_sampled():
-    # full size: 32 x 32768-token verify rows and a 2048-token chunk at 30000;
-    # the oracle computes a sample of rows (first/last token of every
-    # sequence in every head plus random rows)
+def test_config5_parity_full():
+    # full size: 32 x 32768-token verify rows and a 2048-token chunk at
+    # 30000, every one of the 26,496 (token, head) rows against the fp64
+    # oracle (tens of seconds on the host's cores)
     st = workloads.config(5)
     _note(f"config 5: {st.summary()}")
     pools = H.host_pools(st)
     out, gk, gv = run_on_gpu(st, pools=pools)
     check_pool(st, pools, gk, gv)
     del pools, gk, gv
-    check_out(st, out, row_sel=H.sample_rows(st, 400))
+    _note("config 5: oracle over every row ...")
+    check_out(st, out)
 
 
 @pytest.mark.parametrize("flags", [P.PS_PLAN_ALL_DECODE, P.PS_PLAN_ALL_PREFILL])
@@ -224,11 +235,12 @@ def test_block_permutation_is_bit_invariant():
     assert torch.equal(oa, ob)
 
 
-def test_prefix_sharing_is_bit_invariant(monkeypatch):
+def test_prefix_sharing_is_bit_invariant():
     # the same logical contexts, once with the prefix in shared blocks and
-    # once with private copies of it. Without the shared-prefix pass the
-    # physical sharing changes nothing, bit for bit; with it (the default)
-    # the shared step takes the prefix pass and both agree with the oracle.
+    # once with private copies of it: on the default path physical sharing
+    # changes nothing, bit for bit (tinyserve README "Highlights": output
+    # bit-identical with prefix caching on or off). The opt-in shared-prefix
+    # pass sums the prefix in another order; it still matches the oracle.
     shared = workloads.build_step("shared", 41, "bf16", 12, 2, 128, 2048, [1] * 24 + [5] * 8,
                                   (np.arange(32) * 7 + 300).tolist(), prefix_tokens=256)
     private = workloads.build_step("private", 42, "bf16", 12, 2, 128, 2048, shared.q_lens,
@@ -239,11 +251,67 @@ def test_prefix_sharing_is_bit_invariant(monkeypatch):
     assert len(np.unique(private.block_tables[:, 0])) == 32
     os_, _, _ = run_on_gpu(shared)
     op, _, _ = run_on_gpu(private)
-    check_out(shared, os_)
+    assert torch.equal(os_, op), "prefix blocks shared vs private copies changed the output bits"
     check_out(private, op)
-    monkeypatch.setenv("PS_CASCADE", "0")
-    os0, _, _ = run_on_gpu(shared)
-    assert torch.equal(os0, op)
+    osp, _, _ = run_on_gpu(shared, P.PS_PLAN_SHARED_PREFIX)
+    check_out(shared, osp)
+
+
+def _caller_arrays(st, table=None):
+    """The step's index arrays as the caller's own device tensors (not the
+    plan's uploaded metadata)."""
+    ql = st.q_lens.astype(np.int64)
+    qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    nc = st.num_computed.astype(np.int32)
+    ctx = (st.num_computed + st.q_lens).astype(np.int32)
+    bt = np.ascontiguousarray(st.block_tables if table is None else table, dtype=np.int32)
+    return {name: torch.from_numpy(a.copy()).to(DEV) for name, a in
+            (("block_tables", bt), ("query_start_loc", qsl), ("num_computed_tokens", nc), ("context_lens", ctx))}
+
+
+@pytest.mark.parametrize("idx", [1, 3, 4])
+def test_attention_reads_the_callers_arrays(idx):
+    # ps_paged_attention fed the caller's own copies of the index arrays
+    # gives the bits it gives with the plan's; and a table that points at
+    # other blocks holding the same tokens (the pool rearranged, the plan
+    # unchanged) is followed: same bits, and every row against the oracle
+    st = workloads.config(idx)
+    pools = H.host_pools(st)
+    gk = _to_dev_pool(pools[0], st.dtype)
+    gv = _to_dev_pool(pools[1], st.dtype)
+    pool = P.make_pool(gk, gv, st.layer)
+    step = P.PackedStep(st.q_lens, st.num_computed, st.block_tables, st.num_q_heads, pool, DEV)
+    q, k, v = st.q.to(DEV), st.k.to(DEV), st.v.to(DEV)
+    stream = torch.cuda.current_stream()
+    step.reshape_and_cache(k, v, pool, stream)
+    out_plan = torch.full_like(q, float("nan"))
+    step.attention(q, pool, out_plan, st.scale, stream)
+
+    def attend(pool_, arrays):
+        out = torch.full_like(q, float("nan"))
+        P.ps_paged_attention(q, pool_, arrays["block_tables"], st.block_tables.shape[1],
+                             arrays["query_start_loc"], arrays["num_computed_tokens"], arrays["context_lens"],
+                             out, st.num_seqs, st.num_tokens, st.num_q_heads, st.scale, step.plan, step.ws,
+                             step.ws_bytes, stream)
+        return out
+
+    out_own = attend(pool, _caller_arrays(st))
+    torch.cuda.synchronize()
+    assert torch.equal(out_own, out_plan), "caller-owned copies of the arrays changed the output"
+    # move every used block to another id (a permutation of the pool),
+    # and hand the kernels the matching table
+    rng = np.random.default_rng(100 + idx)
+    perm = rng.permutation(st.num_blocks).astype(np.int64)
+    gk2 = torch.empty_like(gk)
+    gv2 = torch.empty_like(gv)
+    pidx = torch.from_numpy(perm).to(DEV)
+    gk2[:, pidx] = gk
+    gv2[:, pidx] = gv
+    moved = np.where(st.block_tables >= 0, perm[np.maximum(st.block_tables, 0)], -1).astype(np.int32)
+    out_moved = attend(P.make_pool(gk2, gv2, st.layer), _caller_arrays(st, moved))
+    torch.cuda.synchronize()
+    assert torch.equal(out_moved, out_plan), "the same tokens through another table changed the output"
+    check_out(st, out_moved.cpu())
 
 
 def test_repeat_is_deterministic():
@@ -289,24 +357,23 @@ def test_empty_step_is_a_noop():
 
 
 @pytest.mark.parametrize("split", [16, 64, 2048])
-def test_forced_splits_merge_exactly(split, monkeypatch):
+def test_forced_splits_merge_exactly(split):
     # short key slices force the split-K path (partials + merge kernel) on
     # small steps, for both kernels
-    monkeypatch.setenv("PS_DECODE_SPLIT", str(split))
-    monkeypatch.setenv("PS_PREFILL_SPLIT", str(split))
-    for flags in (P.PS_PLAN_DEFAULT, P.PS_PLAN_ALL_DECODE, P.PS_PLAN_ALL_PREFILL):
+    for flags in (P.PS_PLAN_DEFAULT, P.PS_PLAN_ALL_DECODE, P.PS_PLAN_ALL_PREFILL, P.PS_PLAN_SEPARATE_LAUNCHES):
         for dt, hq, hkv, d in (("bf16", 12, 2, 128), ("f16", 14, 2, 64), ("f32", 4, 2, 64)):
             st = workloads.random_step(300 + split + hq, dtype=dt, num_q_heads=hq, num_kv_heads=hkv,
                                        head_dim=d, num_seqs=6, max_q=90, max_ctx=700)
             _note(f"split={split} flags={flags} {dt} q_lens={st.q_lens.tolist()}")
-            out, _, _ = run_on_gpu(st, flags=flags)
+            out, _, _ = run_on_gpu(st, flags=flags, decode_split_keys=split,
+                                   prefill_split_keys=max(64, split // 64 * 64))
             check_out(st, out)
 
 
-def _same_as_separate_calls(st, flags):
+def _same_as_separate_calls(st, flags, **options):
     pools = H.host_pools(st)
-    out_f, gk_f, gv_f = run_on_gpu(st, flags=flags, pools=pools)
-    out_s, gk_s, gv_s = run_on_gpu(st, flags=flags, pools=pools, separate=True)
+    out_f, gk_f, gv_f = run_on_gpu(st, flags=flags, pools=pools, **options)
+    out_s, gk_s, gv_s = run_on_gpu(st, flags=flags, pools=pools, separate=True, **options)
     assert np.array_equal(H.bits(out_f), H.bits(out_s)), "ps_step output differs from the two calls"
     assert np.array_equal(gk_f, gk_s) and np.array_equal(gv_f, gv_s), "ps_step pool differs"
     check_pool(st, pools, gk_f, gv_f)
@@ -325,16 +392,15 @@ def test_step_entry_matches_separate_calls(idx):
 
 
 @pytest.mark.parametrize("split", [16, 64])
-def test_step_entry_fused_with_splits_and_row_ranges(split, monkeypatch):
+def test_step_entry_fused_with_splits_and_row_ranges(split):
     # split key slices (only the item holding a sequence's last keys writes
     # them) and, forced onto the decode kernel, sequences with several row
     # ranges per KV head
-    monkeypatch.setenv("PS_DECODE_SPLIT", str(split))
     for dt, hq, hkv, d in (("bf16", 12, 2, 128), ("f16", 14, 2, 64), ("f32", 4, 2, 64), ("f32", 4, 1, 128)):
         st = workloads.random_step(500 + split + hq + d, dtype=dt, num_q_heads=hq, num_kv_heads=hkv,
                                    head_dim=d, num_seqs=7, max_q=40, max_ctx=500)
         _note(f"fused split={split} {dt} D={d} q_lens={st.q_lens.tolist()}")
-        out = _same_as_separate_calls(st, P.PS_PLAN_ALL_DECODE)
+        out = _same_as_separate_calls(st, P.PS_PLAN_ALL_DECODE, decode_split_keys=split)
         check_out(st, out)
 
 

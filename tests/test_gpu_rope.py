@@ -105,8 +105,11 @@ def _check_pools(st, gk, gv, pk, pv, slots, positions, theta):
     _check_rot(got, st.k[torch.from_numpy(np.nonzero(ok)[0])], positions[ok], theta, st.dtype, "pool K")
 
 
+# the last two have more than 512 units (16-byte chunk pairs and v words)
+# per token: a token then takes a workgroup of its own
 CASES = [("f32", 4, 2, 64), ("f32", 2, 1, 128), ("f16", 14, 2, 64), ("f16", 12, 2, 128),
-         ("bf16", 12, 2, 128), ("bf16", 32, 4, 64), ("bf16", 7, 1, 128)]
+         ("bf16", 12, 2, 128), ("bf16", 32, 4, 64), ("bf16", 7, 1, 128),
+         ("bf16", 64, 8, 128), ("f32", 28, 4, 128)]
 
 
 @pytest.mark.parametrize("theta", [1e4, 1e6])

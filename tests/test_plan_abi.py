@@ -23,8 +23,9 @@ def _pool(st, layer=None):
                      DT[st.dtype_name], st.layer if layer is None else layer)
 
 
-def _plan(st, flags=0):
-    return P.ps_plan_step(st.q_lens, st.num_computed, st.block_tables, st.num_q_heads, _pool(st), flags)
+def _plan(st, flags=0, **options):
+    opts = P.plan_options(**options) if options else None
+    return P.ps_plan_step(st.q_lens, st.num_computed, st.block_tables, st.num_q_heads, _pool(st), flags, opts)
 
 
 def test_library_exports_every_declared_symbol():
@@ -251,12 +252,18 @@ def test_split_plan_depends_only_on_logical_lengths():
     assert P.ps_plan_sizes(pa)[1] == P.ps_plan_sizes(pb)[1]
 
 
-def test_shared_prefix_groups(monkeypatch):
+def test_shared_prefix_groups():
     # two groups (10 sequences sharing 320 tokens, 9 sharing 512) among
     # sequences that share nothing, one of which shares only one block
     st = workloads.prefix_groups_step(3, values=False)
     g, hkv = st.num_q_heads // st.num_kv_heads, st.num_kv_heads
-    info = P.ps_plan_get_info(_plan(st))
+    SP = P.PS_PLAN_SHARED_PREFIX
+    # the pass is opt-in: by default physical sharing changes nothing
+    off = P.ps_plan_get_info(_plan(st))
+    assert off["prefix_groups"] == off["prefix_items"] == off["prefill_items"] == 0
+    assert off["decode_items"] == 24 * hkv and off["step_fused"] == 1
+
+    info = P.ps_plan_get_info(_plan(st, SP))
     assert info["prefix_groups"] == 2
     assert info["prefill_items"] == info["prefix_items"] > 0
     assert info["step_fused"] == 1
@@ -265,26 +272,144 @@ def test_shared_prefix_groups(monkeypatch):
     assert info["prefix_items"] >= hkv * (-(-10 * g // 128) + -(-9 * g // 128))
     # every grouped sequence merges its own keys with the prefix pass
     assert info["merge_items"] >= 19 * hkv
+    kinds = P.ps_plan_sequence_kernels(_plan(st, SP), st.num_seqs)
+    assert (kinds == 2).sum() == 19 and (kinds == 0).sum() == st.num_seqs - 19
 
-    monkeypatch.setenv("PS_CASCADE", "0")
-    off = P.ps_plan_get_info(_plan(st))
-    assert off["prefix_groups"] == off["prefix_items"] == off["prefill_items"] == 0
-    assert off["decode_items"] == 24 * hkv and off["step_fused"] == 1
-    monkeypatch.delenv("PS_CASCADE")
-
-    monkeypatch.setenv("PS_CASCADE_MIN_SEQS", "10")   # group B has 9
-    assert P.ps_plan_get_info(_plan(st))["prefix_groups"] == 1
-    monkeypatch.setenv("PS_CASCADE_MIN_SEQS", "11")   # the outlier does not join group A
-    assert P.ps_plan_get_info(_plan(st))["prefix_groups"] == 0
-    monkeypatch.delenv("PS_CASCADE_MIN_SEQS")
-    monkeypatch.setenv("PS_CASCADE_MIN_KEYS", "336")  # group A shares 320 tokens
-    assert P.ps_plan_get_info(_plan(st))["prefix_groups"] == 1
-    monkeypatch.delenv("PS_CASCADE_MIN_KEYS")
+    assert P.ps_plan_get_info(_plan(st, SP, prefix_min_seqs=10))["prefix_groups"] == 1   # group B has 9
+    assert P.ps_plan_get_info(_plan(st, SP, prefix_min_seqs=11))["prefix_groups"] == 0   # the outlier stays out of A
+    assert P.ps_plan_get_info(_plan(st, SP, prefix_min_keys=336))["prefix_groups"] == 1  # group A shares 320
 
     for flags in (P.PS_PLAN_ALL_DECODE, P.PS_PLAN_ALL_PREFILL):
-        assert P.ps_plan_get_info(_plan(st, flags))["prefix_groups"] == 0
+        assert P.ps_plan_get_info(_plan(st, flags | SP))["prefix_groups"] == 0
     # a chunk in the step: the scatter is no longer fused
     wp = workloads.prefix_groups_step(3, with_prefill=True, values=False)
-    iw = P.ps_plan_get_info(_plan(wp))
+    iw = P.ps_plan_get_info(_plan(wp, SP))
     assert iw["prefix_groups"] == 2 and iw["step_fused"] == 0
     assert iw["prefill_items"] > iw["prefix_items"]
+
+
+def test_long_shared_prefix_slices_fit_a_prefill_item():
+    # 256 sequences of 64 query / 8 KV heads sharing a 20480-token prefix:
+    # each (KV head, 128-row chunk) gets one prefix slice by the item-count
+    # rule, but no prefill item may span more keys than it stages block
+    # ids for (16384), so every chunk takes two slices of 10240
+    S, prefix = 256, 20480
+    nc = np.full(S, prefix + 37, dtype=np.int32)
+    st = workloads.build_step("long-prefix", 5, "bf16", 64, 8, 128, 8192, [1] * S, nc.tolist(),
+                              prefix_tokens=prefix, values=False)
+    info = P.ps_plan_get_info(_plan(st, P.PS_PLAN_SHARED_PREFIX))
+    chunks = 8 * (S * 8 // 128)
+    assert info["prefix_groups"] == 1
+    assert info["prefix_items"] == 2 * chunks
+    # an explicit slice length above the limit is refused
+    _expect_error(B.PS_ERR_INVALID_ARGUMENT, _plan, st, P.PS_PLAN_SHARED_PREFIX, prefix_slice_keys=20480,
+                  match="prefix_slice_keys")
+
+
+def test_options_are_validated_and_recorded(monkeypatch):
+    st = workloads.config(3, values=False)
+    INV = B.PS_ERR_INVALID_ARGUMENT
+    for kw in (dict(decode_split_keys=24), dict(decode_split_keys=32768), dict(prefill_split_keys=100),
+               dict(decode_waves=6), dict(prefix_min_seqs=1)):
+        _expect_error(INV, _plan, st, **kw)
+    _expect_error(INV, _plan, st, decode_waves=16, match="head_dim 64")
+    info = P.ps_plan_get_info(_plan(st, decode_split_keys=512, prefill_split_keys=256))
+    assert info["decode_split_keys"] == 512 and info["prefill_split_keys"] == 256
+    assert info["merge_items"] > 0 and info["workspace_rows"] > 0
+    dflt = P.ps_plan_get_info(_plan(st))
+    assert dflt["mixed_launch"] == 1
+    assert P.ps_plan_get_info(_plan(st, P.PS_PLAN_SEPARATE_LAUNCHES))["mixed_launch"] == 0
+    # nothing in the environment changes a plan
+    for name in ("PS_DECODE_SPLIT", "PS_PREFILL_SPLIT", "PS_CASCADE", "PS_DECODE_WAVES", "PS_MIXED"):
+        monkeypatch.setenv(name, "64")
+    again = P.ps_plan_get_info(_plan(st))
+    for key in ("decode_items", "prefill_items", "merge_items", "decode_split_keys", "prefill_split_keys",
+                "decode_waves", "mixed_launch", "prefix_groups"):
+        assert again[key] == dflt[key], key
+
+
+def test_sequence_kernels():
+    st = workloads.config(3, values=False)
+    kinds = P.ps_plan_sequence_kernels(_plan(st), st.num_seqs)
+    g = st.num_q_heads // st.num_kv_heads
+    np.testing.assert_array_equal(kinds, np.where(g * st.q_lens > 32, 1, 0))
+    assert (P.ps_plan_sequence_kernels(_plan(st, P.PS_PLAN_ALL_PREFILL), st.num_seqs) == 1).all()
+
+
+def _fixed(**kw):
+    base = dict(max_seqs=64, max_tokens=64, max_query_len=1)
+    base.update(kw)
+    return base
+
+
+def test_fixed_shape_layout_depends_only_on_capacities():
+    # two decode steps of different lengths and sequence counts planned to
+    # one fixed shape: same metadata and workspace sizes, same launch
+    # counts, and idle items pad the work lists
+    c2 = workloads.config(2, values=False)
+    a = workloads.build_step("c2-width64", 12, "f16", 14, 2, 64, 4096, c2.q_lens, c2.num_computed,
+                             table_width=64, values=False)
+    b = workloads.build_step("c2-next", 13, "f16", 14, 2, 64, 4096, [1] * 50,
+                             np.random.default_rng(3).integers(15, 700, 50).tolist(),
+                             table_width=64, values=False)
+    F = P.PS_PLAN_FIXED_SHAPE
+    pa = _plan(a, F, **_fixed())
+    pb = _plan(b, F, **_fixed())
+    assert P.ps_plan_sizes(pa) == P.ps_plan_sizes(pb)
+    ia, ib = P.ps_plan_get_info(pa), P.ps_plan_get_info(pb)
+    for key in ("decode_items", "merge_items", "decode_row_tiles", "decode_waves", "workspace_rows"):
+        assert ia[key] == ib[key], key
+    assert ia["decode_items"] == 128 and ia["active_decode_items"] == 128
+    assert ib["active_decode_items"] == 100 and ib["step_fused"] == 1
+    # too many sequences, too long a query, a prefill route: refused
+    INV = B.PS_ERR_INVALID_ARGUMENT
+    _expect_error(INV, _plan, a, F, **_fixed(max_seqs=63), match="exceeds")
+    _expect_error(INV, _plan, a, F, **_fixed(max_query_len=5), match="rows")
+    _expect_error(INV, _plan, a, F | P.PS_PLAN_ALL_PREFILL, **_fixed(), match="FIXED")
+    _expect_error(INV, _plan, a, F | P.PS_PLAN_SHARED_PREFIX, **_fixed(), match="FIXED")
+    # key splits need merge capacity
+    _expect_error(INV, _plan, a, F, **_fixed(decode_split_keys=64), match="fixed shape holds")
+    ok = P.ps_plan_get_info(_plan(a, F, **_fixed(decode_split_keys=64, max_decode_items=2048,
+                                                  max_merge_items=1024, max_workspace_rows=16384)))
+    assert ok["merge_items"] == 1024 and 0 < ok["active_merge_items"] <= 1024
+
+
+def _c5_like_tables(num_blocks, seed=0):
+    rng = np.random.default_rng(seed)
+    q_lens = np.array([5] * 32 + [2048], dtype=np.int32)
+    nc = np.array([32763] * 32 + [30000], dtype=np.int32)
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    bt = np.full((33, 2048), -1, dtype=np.int32)
+    off = 0
+    for s in range(33):
+        nb = -(-(int(nc[s]) + int(q_lens[s])) // 16)
+        bt[s, :nb] = perm[off:off + nb]
+        off += nb
+    return q_lens, nc, bt
+
+
+def test_planner_cost_follows_the_step_not_the_pool():
+    # the same C5-shaped step (67k table entries) over pools of 100k and of
+    # 1M blocks: the plans agree, and the larger pool does not make the
+    # planner walk or clear pool-sized state
+    times = {}
+    for nb in (100_000, 1_000_000):
+        q_lens, nc, bt = _c5_like_tables(nb)
+        pool = P.ps_pool(0, 0, 1, nb, 16, 2, 128, P.PS_BF16, 0)
+        best, info = float("inf"), None
+        for _ in range(5):
+            plan = P.ps_plan_step(q_lens, nc, bt, 12, pool)
+            info = P.ps_plan_get_info(plan)
+            best = min(best, info["plan_us"])
+        times[nb] = best
+        assert info["kv_bytes_unique"] == info["kv_bytes_decode"] + info["kv_bytes_prefill"]
+        # validation still sees every entry: a duplicate near the top of the pool
+        bt2 = bt.copy()
+        bt2[7, 100] = bt2[7, 3]
+        _expect_error(B.PS_ERR_INVALID_ARGUMENT, P.ps_plan_step, q_lens, nc, bt2, 12, pool, match="twice")
+        bt2 = bt.copy()
+        bt2[32, 1999] = bt2[4, 10]   # the chunk appends into a block another table reads
+        _expect_error(B.PS_ERR_INVALID_ARGUMENT, P.ps_plan_step, q_lens, nc, bt2, 12, pool, match="share")
+    # generous bound (shared CI hosts are noisy): a pool-sized pass would be
+    # 10x; the step-sized work is a small constant factor at most
+    assert times[1_000_000] < 6 * times[100_000] + 2000, times
