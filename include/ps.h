@@ -350,6 +350,30 @@ ps_status ps_step(const void *q, const void *k, const void *v, const int32_t *sl
                   size_t workspace_bytes, void *stream);
 
 /*
+ * ps_step for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments and results as ps_step (bit for bit), without the
+ * workspace: the split-K partials go to a static device array of
+ * PS_STATIC_WORKSPACE_BYTES that the library holds on each GPU it runs on
+ * until the process ends. A plan whose workspace (ps_plan_sizes) exceeds
+ * it is refused with PS_ERR_WORKSPACE_TOO_SMALL before anything is
+ * enqueued (longer key splits, ps_plan_options, shrink it). The call
+ * allocates nothing; its first call on a device (which must be current)
+ * looks up that device's array, so make it outside a graph capture. All
+ * calls on one GPU share its array: calls that overlap in time on that GPU
+ * (other streams, other threads) race on it and must be serialised by the
+ * caller. Nothing needs to start zeroed: every partial is written before
+ * it is read.
+ */
+#define PS_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
+
+ps_status ps_step_no_alloc(const void *q, const void *k, const void *v, const int32_t *slot_mapping,
+                           const ps_pool *pool, const int32_t *block_tables, int32_t block_table_stride,
+                           const int32_t *query_start_loc, const int32_t *num_computed_tokens,
+                           const int32_t *context_lens, void *out, int32_t num_seqs, int32_t num_tokens,
+                           int32_t num_q_heads, float scale, const ps_plan *plan, void *stream);
+
+/*
  * Copy whole blocks between two pools of the same layout (num_layers,
  * block_size, num_kv_heads, head_dim, dtype; num_blocks may differ): for
  * every pair i and every layer, block src_blocks[i] of (src->k, src->v) is

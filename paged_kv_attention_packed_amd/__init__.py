@@ -11,5 +11,5 @@ from ._binding import (  # noqa: F401
     plan_options, ps_abi_version, ps_copy_blocks, ps_paged_attention, ps_plan_device_arrays,
     ps_plan_get_info, ps_plan_host_arrays, ps_plan_sequence_kernels, ps_plan_sizes, ps_plan_step,
     ps_plan_upload, ps_pool, ps_reshape_and_cache, ps_rope_reshape_and_cache, ps_spec_verify,
-    ps_spec_verify_workspace_bytes, ps_step, status_string)
+    ps_spec_verify_workspace_bytes, ps_step, ps_step_no_alloc, status_string)
 from .step import PackedStep  # noqa: F401

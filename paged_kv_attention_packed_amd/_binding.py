@@ -34,7 +34,7 @@ EXPORTED = [
     "ps_plan_step", "ps_plan_sizes", "ps_plan_upload", "ps_plan_device_arrays",
     "ps_plan_host_arrays", "ps_plan_get_info", "ps_plan_sequence_kernels", "ps_plan_destroy",
     "ps_reshape_and_cache",
-    "ps_paged_attention", "ps_step", "ps_copy_blocks", "ps_rope_reshape_and_cache", "ps_spec_verify",
+    "ps_paged_attention", "ps_step", "ps_step_no_alloc", "ps_copy_blocks", "ps_rope_reshape_and_cache", "ps_spec_verify",
     "ps_spec_verify_workspace_bytes", "ps_status_string", "ps_last_error_message", "ps_abi_version",
 ]
 
@@ -130,6 +130,9 @@ lib.ps_paged_attention.argtypes = [_vp, ctypes.POINTER(ps_pool), _vp, ctypes.c_i
 lib.ps_step.restype = ctypes.c_int32
 lib.ps_step.argtypes = [_vp, _vp, _vp, _vp, ctypes.POINTER(ps_pool), _vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _vp, _vp, _sz, _vp]
+lib.ps_step_no_alloc.restype = ctypes.c_int32
+lib.ps_step_no_alloc.argtypes = [_vp, _vp, _vp, _vp, ctypes.POINTER(ps_pool), _vp, ctypes.c_int32, _vp, _vp, _vp,
+                                 _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _vp, _vp]
 lib.ps_copy_blocks.restype = ctypes.c_int32
 lib.ps_copy_blocks.argtypes = [ctypes.POINTER(ps_pool), ctypes.POINTER(ps_pool), _vp, _vp, ctypes.c_int32, _vp]
 lib.ps_rope_reshape_and_cache.restype = ctypes.c_int32
@@ -286,6 +289,18 @@ def ps_step(q, k, v, slot_mapping, pool: ps_pool, block_tables, block_table_stri
                        block_table_stride, _ptr(query_start_loc), _ptr(num_computed_tokens),
                        _ptr(context_lens), _ptr(out), num_seqs, num_tokens, num_q_heads, scale, plan.handle,
                        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+PS_STATIC_WORKSPACE_BYTES = 128 << 20
+
+
+def ps_step_no_alloc(q, k, v, slot_mapping, pool: ps_pool, block_tables, block_table_stride: int,
+                     query_start_loc, num_computed_tokens, context_lens, out, num_seqs: int, num_tokens: int,
+                     num_q_heads: int, scale: float, plan: Plan, stream=None):
+    _check(lib.ps_step_no_alloc(_ptr(q), _ptr(k), _ptr(v), _ptr(slot_mapping), ctypes.byref(pool),
+                                _ptr(block_tables), block_table_stride, _ptr(query_start_loc),
+                                _ptr(num_computed_tokens), _ptr(context_lens), _ptr(out), num_seqs, num_tokens,
+                                num_q_heads, scale, plan.handle, _stream(stream)))
 
 
 def ps_copy_blocks(src: ps_pool, dst: ps_pool, src_blocks, dst_blocks, num_pairs: int, stream=None):

@@ -224,6 +224,9 @@ inline size_t ps_spec_workspace(int64_t num_seqs, int64_t vocab) {
 int ps_launch_scatter(const void *k, const void *v, const int32_t *slot_mapping,
                       int32_t num_tokens, const ps_pool *pool, void *stream);
 int ps_launch_attention(const ps_attn_launch &a, void *stream);
+// The current device's static split-K workspace (PS_STATIC_WORKSPACE_BYTES),
+// looked up once per device (ps_kernels.hip). Returns hipError_t as int.
+int ps_static_workspace(void **ptr);
 int ps_prefill_rows(int dtype);  // packed rows per prefill work item
 int ps_launch_copy_blocks(const ps_pool *src, const ps_pool *dst, const int32_t *src_blocks,
                           const int32_t *dst_blocks, int32_t num_pairs, void *stream);

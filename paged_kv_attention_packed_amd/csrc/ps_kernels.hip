@@ -30,6 +30,7 @@
 #include <stdint.h>
 
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "ps_internal.h"
@@ -1530,6 +1531,36 @@ int ps_launch_attention(const ps_attn_launch &a, void *stream) {
         default: e = launch_attention_d<TBF16>(a, st); break;
     }
     return (int)e;
+}
+
+// ---------------------------------------------------------------------------
+// Static split-K workspace of ps_step_no_alloc: one array per GPU, held
+// until the process ends. In host code `scratch` only names the symbol; its
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current, and only that address is handed to kernels.
+
+static __device__ __align__(256) uint8_t scratch[PS_STATIC_WORKSPACE_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+int ps_static_workspace(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return (int)g_scratch_err[dev];
+    *ptr = g_scratch_ptr[dev];
+    return 0;
 }
 
 int ps_launch_scatter(const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,

@@ -939,3 +939,25 @@ extern "C" ps_status ps_step(const void *q, const void *k, const void *v, const 
     if (err != 0) return ps_fail(PS_ERR_HIP, "step launch: %s", ps_hip_error_string(err));
     return PS_OK;
 }
+
+extern "C" ps_status ps_step_no_alloc(const void *q, const void *k, const void *v, const int32_t *slot_mapping,
+                                      const ps_pool *pool, const int32_t *block_tables,
+                                      int32_t block_table_stride, const int32_t *query_start_loc,
+                                      const int32_t *num_computed_tokens, const int32_t *context_lens, void *out,
+                                      int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, float scale,
+                                      const ps_plan *plan, void *stream) {
+    if (!plan) return ps_fail(PS_ERR_INVALID_ARGUMENT, "plan is NULL");
+    const size_t need = ps_workspace_layout(plan->ws_rows, plan->D).bytes;
+    if (need > PS_STATIC_WORKSPACE_BYTES)
+        return ps_fail(PS_ERR_WORKSPACE_TOO_SMALL,
+                       "step needs %zu bytes of split-K workspace, the static workspace holds %zu "
+                       "(plan longer key splits)", need, (size_t)PS_STATIC_WORKSPACE_BYTES);
+    void *ws = nullptr;
+    if (need > 0) {
+        const int err = ps_static_workspace(&ws);
+        if (err != 0) return ps_fail(PS_ERR_HIP, "static workspace: %s", ps_hip_error_string(err));
+    }
+    return ps_step(q, k, v, slot_mapping, pool, block_tables, block_table_stride, query_start_loc,
+                   num_computed_tokens, context_lens, out, num_seqs, num_tokens, num_q_heads, scale, plan, ws,
+                   need, stream);
+}
