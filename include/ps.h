@@ -150,7 +150,11 @@ typedef struct {
     int32_t max_decode_items;    /* 0 = max_seqs * num_kv_heads */
     int32_t max_merge_items;     /* 0: no key splits allowed */
     int32_t max_workspace_rows;  /* split-K partial rows (0 with no splits) */
-    int32_t reserved[4];         /* must be 0 */
+    int32_t decode_walk_rotation; /* 1: each decode item starts its walk over its key tiles at an
+                                    item-dependent tile (helps when many items read the same
+                                    shared blocks); 0 (default): at its first tile. A function of
+                                    the item only, never of physical sharing */
+    int32_t reserved[3];         /* must be 0 */
 } ps_plan_options;
 
 /*
@@ -251,6 +255,7 @@ typedef struct {
     /* the choices the planner made (options resolved) */
     int32_t decode_split_keys, prefill_split_keys, decode_waves, mixed_launch;
     int32_t active_decode_items, active_merge_items;  /* items that do work (fixed shape pads) */
+    int32_t decode_walk_rotation, reserved2;
     int64_t workspace_rows;                     /* split-K partial rows */
     double plan_us;                             /* host time ps_plan_step took */
 } ps_plan_info;

@@ -159,8 +159,10 @@ ps_status check_options(const ps_plan_options &o, uint32_t flags, const ps_pool 
     if (o.prefix_min_seqs < 0 || o.prefix_min_seqs == 1 || o.prefix_min_keys < 0 ||
         (o.prefix_min_keys > 0 && o.prefix_min_keys < PS_BLOCK))
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "prefix_min_seqs must be 0 or >= 2, prefix_min_keys 0 or >= 16");
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 3; ++i)
         if (o.reserved[i] != 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "reserved option fields must be 0");
+    if (o.decode_walk_rotation != 0 && o.decode_walk_rotation != 1)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "decode_walk_rotation %d: 0 or 1", o.decode_walk_rotation);
     if (flags & PS_PLAN_FIXED_SHAPE) {
         if ((flags & 3) == PS_PLAN_ALL_PREFILL || (flags & PS_PLAN_SHARED_PREFIX))
             return ps_fail(PS_ERR_INVALID_ARGUMENT,
@@ -281,35 +283,44 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
             }
         } clear{bm, q_lens, num_computed_tokens, block_tables, S, block_table_stride, NB, n_entries};
         constexpr uint32_t kShared = 1u << 5;
-        for (int32_t s = 0; s < S; ++s) {
-            const int32_t *row = block_tables + (int64_t)s * block_table_stride;
-            const int64_t ctx = (int64_t)num_computed_tokens[s] + q_lens[s];
-            const int64_t nblk = ceil_div(ctx, PS_BLOCK);
-            const uint32_t tag = (uint32_t)(s + 1) << 6;
-            constexpr int64_t kAhead = 16;
-            for (int64_t b = 0; b < std::min(nblk, kAhead); ++b)
-                if (row[b] >= 0 && row[b] < NB) bm.prefetch(row[b]);
-            for (int64_t b = 0; b < nblk; ++b) {
-                const int32_t id = row[b];
-                if (id < 0 || id >= NB)
-                    return ps_fail(PS_ERR_INVALID_ARGUMENT, "block_tables[%d][%lld] = %d outside [0, %d)", s,
-                                   (long long)b, id, NB);
-                if (b + kAhead < nblk && row[b + kAhead] >= 0 && row[b + kAhead] < NB) bm.prefetch(row[b + kAhead]);
-                const uint32_t ntok = (uint32_t)std::min<int64_t>(PS_BLOCK, ctx - b * PS_BLOCK);
-                uint32_t &m = bm.at(id);
-                if (m == 0u) {
-                    m = tag | ntok;
-                    kv_rows_unique += ntok;
-                } else {
-                    if ((m >> 6) == (uint32_t)(s + 1))
+        // one pass over every table entry the step covers, branch-free but
+        // for the (rare) errors; `slot` gives the mark of a block id
+        auto scan = [&](auto slot, auto prefetch) -> ps_status {
+            int64_t uniq = 0;
+            for (int32_t s = 0; s < S; ++s) {
+                const int32_t *row = block_tables + (int64_t)s * block_table_stride;
+                const int64_t ctx = (int64_t)num_computed_tokens[s] + q_lens[s];
+                const int64_t nblk = ceil_div(ctx, PS_BLOCK);
+                const uint32_t tag = (uint32_t)(s + 1) << 6;
+                constexpr int64_t kAhead = 16;
+                for (int64_t b = 0; b < std::min(nblk, kAhead); ++b) prefetch(row[b]);
+                for (int64_t b = 0; b < nblk; ++b) {
+                    const int32_t id = row[b];
+                    if ((uint32_t)id >= (uint32_t)NB)
+                        return ps_fail(PS_ERR_INVALID_ARGUMENT, "block_tables[%d][%lld] = %d outside [0, %d)", s,
+                                       (long long)b, id, NB);
+                    if (b + kAhead < nblk) prefetch(row[b + kAhead]);
+                    const uint32_t ntok = (uint32_t)std::min<int64_t>(PS_BLOCK, ctx - b * PS_BLOCK);
+                    uint32_t &m = slot(id);
+                    const uint32_t m0 = m;
+                    if ((m0 >> 6) == (uint32_t)(s + 1))
                         return ps_fail(PS_ERR_INVALID_ARGUMENT, "block %d appears twice in the table of sequence %d",
                                        id, s);
-                    const uint32_t old = m & 31u;
-                    kv_rows_unique += ntok > old ? ntok - old : 0;
-                    m = tag | kShared | std::max(ntok, old);
+                    const uint32_t old = m0 & 31u;
+                    const uint32_t seen = m0 != 0u;
+                    uniq += ntok > old ? ntok - old : 0;
+                    m = tag | (seen << 5) | std::max(ntok, old);
                 }
             }
-        }
+            kv_rows_unique = uniq;
+            return PS_OK;
+        };
+        uint32_t *const dense = bm.dense.data();
+        const ps_status scanned =
+            bm.is_dense ? scan([dense](int32_t id) -> uint32_t & { return dense[(size_t)id]; }, [](int32_t) {})
+                        : scan([&](int32_t id) -> uint32_t & { return bm.at(id); },
+                               [&](int32_t id) { if ((uint32_t)id < (uint32_t)NB) bm.prefetch(id); });
+        if (scanned != PS_OK) return scanned;
         for (int32_t s = 0; s < S; ++s) {
             const int32_t *row = block_tables + (int64_t)s * block_table_stride;
             const int64_t c = num_computed_tokens[s], ctx = c + q_lens[s];
@@ -508,7 +519,12 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                         it.key_end = (int32_t)bounds[i + 1];
                         it.partial_row = nsplit > 1 ? (int32_t)(base + (npk + i) * (r1 - r0)) : -1;
                         it.flags = r1 == rows && i == ns - 1 ? PS_ITEM_WRITES_NEW : 0;
-                        if (d) {
+                        if (d && opt.decode_walk_rotation) {
+                            // walks start at an item-dependent tile, so that
+                            // items reading the same blocks do not all ask for
+                            // the same lines at once (measured on MI355X:
+                            // 256 sequences behind one shared prefix -4%,
+                            // 64 short unshared decodes +16%: off by default)
                             const int64_t ntiles = ceil_div(it.key_end - it.key_begin, PS_DEC_TILE);
                             it.rot = ntiles > 1 ? (int32_t)((dec.size() * 13) % (size_t)ntiles) : 0;
                         }
@@ -713,6 +729,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         I.prefill_split_keys = (int32_t)pre_split;
         I.decode_waves = p->dec_waves;
         I.mixed_launch = p->mixed;
+        I.decode_walk_rotation = opt.decode_walk_rotation;
         I.active_decode_items = act_dec;
         I.active_merge_items = act_mrg;
         I.workspace_rows = cap_ws;

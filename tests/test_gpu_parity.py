@@ -253,6 +253,11 @@ def test_prefix_sharing_is_bit_invariant():
     op, _, _ = run_on_gpu(private)
     assert torch.equal(os_, op), "prefix blocks shared vs private copies changed the output bits"
     check_out(private, op)
+    # walks rotated per item (a function of the item, not of the sharing)
+    osr, _, _ = run_on_gpu(shared, decode_walk_rotation=1)
+    opr, _, _ = run_on_gpu(private, decode_walk_rotation=1)
+    assert torch.equal(osr, opr), "rotated walks: sharing changed the output bits"
+    check_out(shared, osr)
     osp, _, _ = run_on_gpu(shared, P.PS_PLAN_SHARED_PREFIX)
     check_out(shared, osp)
 
