@@ -379,15 +379,21 @@ __device__ inline void dma16_sv(const void *base, uint32_t voff, uint32_t lds_of
 #pragma clang diagnostic pop
 
 // 16-byte chunk position of `chunk` in key row `row`: XOR-swizzled so that
-// 16 consecutive lanes reading one chunk of 16 consecutive rows, or 16
-// chunks of one row, touch 16 different 16-byte bank groups (256 bytes)
+// the operand reads of a tile do not pile onto a few LDS banks.
 //
-// 256-byte (and longer) rows: chunk ^ f(row), f a bijection of row % 16
-// that is even for each aligned group of 4 rows, so the transposed V reads
-// (2 adjacent chunks of 4 adjacent rows) also land in 8 distinct groups.
+// 256-byte (and longer) rows: chunk ^ f(row), f(r) = (r ^ 2r) mod 16, an
+// invertible XOR-linear map of row % 16. Three read shapes use these rows:
+// one chunk of 16 rows per 16 lanes (K operands, ds_read_b128), 8 bytes of
+// 2 adjacent chunks of 4 adjacent rows per 16 lanes (V operands, transposing
+// reads) and whole rows per 16 lanes (V rows of the decode kernel). gfx950's
+// lane-to-bank pairing for these reads is not documented; timed on MI355X
+// (one 64-row tile read over and over, 4 workgroups per CU), this f runs all
+// three at 440-490 B/ns per CU, where the row-XOR keys tried besides it
+// (r, (r mod 8) << 1 with bit 3 in bit 0, no swizzle, and others) leave at
+// least one of them at 290-300 or below.
 template <int ROWB>
 __device__ inline int swz(int chunk, int row) {
-    if constexpr (ROWB >= 256) return chunk ^ (((row & 7) << 1) | ((row >> 3) & 1));
+    if constexpr (ROWB >= 256) return chunk ^ ((row ^ (row << 1)) & 15);
     else return chunk ^ ((row >> 1) & 7);  // 128-byte rows: two rows share 256 bytes
 }
 
