@@ -773,8 +773,8 @@ def main():
         "host_plan_us": round(min(plan_us), 1),
         "host_plan_call_us": round(host_call_us, 1),
         "plan": {key: info[key] for key in ("decode_items", "prefill_items", "merge_items", "decode_split_keys",
-                                            "prefill_split_keys", "decode_waves", "mixed_launch", "step_fused",
-                                            "workspace_rows", "flags")},
+                                            "prefill_split_keys", "decode_waves", "mixed_launch",
+                                            "decode_stream_kv", "step_fused", "workspace_rows", "flags")},
         "pool_copies": nrot,
         "launch": "eager" if args.eager else "hip-graph replay",
         "gpu": torch.cuda.get_device_name(0),

@@ -154,7 +154,13 @@ typedef struct {
                                     item-dependent tile (helps when many items read the same
                                     shared blocks); 0 (default): at its first tile. A function of
                                     the item only, never of physical sharing */
-    int32_t reserved[3];         /* must be 0 */
+    int32_t decode_stream_kv;    /* cache policy of the decode kernel's K/V loads: 0 = planner's
+                                    choice, 1 = non-temporal (streamed), 2 = cached. Results are the
+                                    same either way; the planner streams when no physical block is
+                                    read by two sequences of the step and the decode sequences' K/V
+                                    exceed 256 MiB (MI355X's last-level cache: none of it would
+                                    still be cached at its next use), never for PS_PLAN_FIXED_SHAPE */
+    int32_t reserved[2];         /* must be 0 */
 } ps_plan_options;
 
 /*
@@ -255,7 +261,8 @@ typedef struct {
     /* the choices the planner made (options resolved) */
     int32_t decode_split_keys, prefill_split_keys, decode_waves, mixed_launch;
     int32_t active_decode_items, active_merge_items;  /* items that do work (fixed shape pads) */
-    int32_t decode_walk_rotation, reserved2;
+    int32_t decode_walk_rotation;
+    int32_t decode_stream_kv;                   /* 1: decode K/V loads are non-temporal */
     int64_t workspace_rows;                     /* split-K partial rows */
     double plan_us;                             /* host time ps_plan_step took */
 } ps_plan_info;

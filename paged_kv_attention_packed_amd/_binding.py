@@ -58,8 +58,9 @@ class ps_plan_options(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "decode_split_keys", "prefill_split_keys", "decode_waves", "prefix_min_seqs",
         "prefix_min_keys", "prefix_slice_keys", "max_seqs", "max_tokens", "max_query_len",
-        "max_decode_items", "max_merge_items", "max_workspace_rows", "decode_walk_rotation")] + [
-        ("reserved", ctypes.c_int32 * 3)]
+        "max_decode_items", "max_merge_items", "max_workspace_rows", "decode_walk_rotation",
+        "decode_stream_kv")] + [
+        ("reserved", ctypes.c_int32 * 2)]
 
 
 def plan_options(**kw) -> ps_plan_options:
@@ -83,7 +84,7 @@ class ps_plan_info(ctypes.Structure):
         (n, ctypes.c_int32) for n in ("prefix_groups", "prefix_items", "step_fused", "flags",
                                       "decode_split_keys", "prefill_split_keys", "decode_waves",
                                       "mixed_launch", "active_decode_items", "active_merge_items",
-                                      "decode_walk_rotation", "reserved2")] + [
+                                      "decode_walk_rotation", "decode_stream_kv")] + [
         ("workspace_rows", ctypes.c_int64), ("plan_us", ctypes.c_double)]
 
     def as_dict(self) -> dict:

@@ -143,6 +143,7 @@ struct ps_attn_launch {
     int32_t decode_row_tiles;
     int32_t decode_waves;   // waves per decode workgroup (4, 8 or 16)
     int32_t mixed;          // decode and prefill items share one launch
+    int32_t stream_kv;      // decode items load K/V non-temporally
     float scale_log2;       // softmax scale * log2(e)
     // g = num_q_heads / num_kv_heads, and r / g for 0 <= r < 2^31 as
     // (r * g_magic) >> g_shift (see ps_group_divisor)

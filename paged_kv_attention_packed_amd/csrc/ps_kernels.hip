@@ -120,18 +120,26 @@ __device__ inline float xor_sum(float x) {
     return a + b;
 }
 
+// A vector load; STREAM: marked non-temporal (streamed past the caches' normal
+// allocation: for data the step reads once)
+template <bool STREAM, class V>
+__device__ inline V load_vec(const V *p) {
+    if constexpr (STREAM) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
 // N consecutive 32-bit words from a 4*N-byte aligned address
-template <int N>
+template <int N, bool STREAM = false>
 __device__ inline void load_words(const void *p, uint32_t (&w)[N]) {
     if constexpr (N == 2) {
-        const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
+        const u32x2 x = load_vec<STREAM>(reinterpret_cast<const u32x2 *>(p));
         w[0] = x[0];
         w[1] = x[1];
     } else {
         static_assert(N % 4 == 0, "word count");
 #pragma unroll
         for (int i = 0; i < N / 4; ++i) {
-            const u32x4 x = reinterpret_cast<const u32x4 *>(p)[i];
+            const u32x4 x = load_vec<STREAM>(reinterpret_cast<const u32x4 *>(p) + i);
             w[4 * i + 0] = x[0];
             w[4 * i + 1] = x[1];
             w[4 * i + 2] = x[2];
@@ -363,17 +371,25 @@ __global__ __launch_bounds__(256) void ps_copy_blocks_kernel(const u32x4 *__rest
 // LDS destination; nothing else on gfx950 reads it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is a reserved register: the clobber is the point
+template <bool STREAM = false>
 __device__ inline void dma16(const void *src, uint8_t *lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const uint32_t off = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(off) : "m0");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(off) : "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(off) : "m0");
 #endif
 }
 // Same, addressed as a scalar base plus a 32-bit per-lane byte offset.
+template <bool STREAM = false>
 __device__ inline void dma16_sv(const void *base, uint32_t voff, uint32_t lds_off) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_off) : "m0");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "s"(lds_off) : "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_off) : "m0");
 #endif
 }
 #pragma clang diagnostic pop
@@ -408,7 +424,9 @@ struct DecodeLds {
     int32_t bt[PS_DEC_MAX_SPLIT / PS_BLOCK];  // the item's block ids
 };
 
-template <class DT, int D, int RT, int NW>
+// STREAM: the item's K/V loads from the pool are non-temporal (the planner's
+// choice for steps that read each block once and more than the caches hold)
+template <class DT, int D, int RT, int NW, bool STREAM>
 __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, DecodeLds<DT, D, RT, NW> &sh) {
     using G = Geo<DT, D>;
     using T = typename DT::T;
@@ -564,13 +582,13 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
                 if (sb == 0 || has1) {
 #pragma unroll
                     for (int u = 0; u < KU4; ++u)
-                        kf[buf][sb][u] = *reinterpret_cast<const u32x4 *>(kb_pool + koff + 64 * u);
+                        kf[buf][sb][u] = load_vec<STREAM>(reinterpret_cast<const u32x4 *>(kb_pool + koff + 64 * u));
                 } else {
 #pragma unroll
                     for (int u = 0; u < KU4; ++u) kf[buf][sb][u] = u32x4{0u, 0u, 0u, 0u};
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) load_words<VW>(vb_pool + voff[i], vr[buf][sb * 4 + i]);
+                for (int i = 0; i < 4; ++i) load_words<VW, STREAM>(vb_pool + voff[i], vr[buf][sb * 4 + i]);
             } else {
                 // the block holds keys of this step: rows in [new_lo, ke)
                 // come from k_new / v_new (key position p is packed token
@@ -581,7 +599,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
                                                                 : kb_pool + koff;
 #pragma unroll
                     for (int u = 0; u < KU4; ++u)
-                        kf[buf][sb][u] = *reinterpret_cast<const u32x4 *>(src + 64 * u);
+                        kf[buf][sb][u] = load_vec<STREAM>(reinterpret_cast<const u32x4 *>(src + 64 * u));
                 } else {
 #pragma unroll
                     for (int u = 0; u < KU4; ++u) kf[buf][sb][u] = u32x4{0u, 0u, 0u, 0u};
@@ -591,7 +609,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
                     const int pos = kbk + 4 * q4 + i;
                     const char *src = pos >= new_lo && pos < ke ? vnew + new_row(pos) * rsb + EPL * c * ELT
                                                                 : vb_pool + voff[i];
-                    load_words<VW>(src, vr[buf][sb * 4 + i]);
+                    load_words<VW, STREAM>(src, vr[buf][sb * 4 + i]);
                 }
             }
         }
@@ -717,13 +735,13 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
                 const uint64_t ubase =
                     ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
                     (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
-                dma16_sv(reinterpret_cast<const void *>(ubase), (uint32_t)(((rr & 15) * (int)rs + chunk) * ELT),
+                dma16_sv<STREAM>(reinterpret_cast<const void *>(ubase), (uint32_t)(((rr & 15) * (int)rs + chunk) * ELT),
                          slot_lds + i * 1024);
             } else {
                 const int pos = k0 + rr;
                 const T *src = pos >= new_lo && pos < ke ? (kv ? vn : kn) + new_row(pos) * rs + chunk
                                                          : pool + (blk * 16 + (rr & 15)) * rs + chunk;
-                dma16(src, slot + i * 1024);
+                dma16<STREAM>(src, slot + i * 1024);
             }
         }
     };
@@ -880,10 +898,10 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     }
 }
 
-template <class DT, int D, int RT, int NW>
+template <class DT, int D, int RT, int NW, bool STREAM>
 __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(const ps_attn_launch a) {
     __shared__ DecodeLds<DT, D, RT, NW> L;
-    decode_item<DT, D, RT, NW>(a, blockIdx.x, L);
+    decode_item<DT, D, RT, NW, STREAM>(a, blockIdx.x, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -1378,7 +1396,7 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
 // every round of resident items keeps some HBM reads running under the
 // MFMA work, instead of all of them running in the first rounds (C5 -1%;
 // with fewer prefill items it is slower: C3 +2%, C4 +17%).
-template <class DT, int D, int RT>
+template <class DT, int D, int RT, bool STREAM>
 __global__ __launch_bounds__(256, 2) void ps_mixed_kernel(const ps_attn_launch a) {
     __shared__ union {
         DecodeLds<DT, D, RT, 4> d;
@@ -1404,7 +1422,7 @@ __global__ __launch_bounds__(256, 2) void ps_mixed_kernel(const ps_attn_launch a
         dec = b < 2 * m ? (b & 1) == 0 : nd > np;
         idx = b < 2 * m ? b >> 1 : m + (b - 2 * m);
     }
-    if (dec) decode_item<DT, D, RT, 4>(a, idx, L.d);
+    if (dec) decode_item<DT, D, RT, 4, STREAM>(a, idx, L.d);
     else prefill_item<DT, D, PS_PRE_TILE, 2, 32>(a, idx, L.p);
 }
 
@@ -1486,26 +1504,34 @@ hipError_t launch_attention_t(const ps_attn_launch &a, hipStream_t st) {
     if constexpr (DT::ELT == 2) {
         if (a.n_decode > 0 && a.n_prefill > 0 && a.mixed) {
             const dim3 grid(a.n_decode + a.n_prefill), block(256);
-            if (a.decode_row_tiles == 2)
-                hipLaunchKernelGGL((ps_mixed_kernel<DT, D, 2>), grid, block, 0, st, a);
-            else
-                hipLaunchKernelGGL((ps_mixed_kernel<DT, D, 1>), grid, block, 0, st, a);
+            if (a.decode_row_tiles == 2) {
+                if (a.stream_kv) hipLaunchKernelGGL((ps_mixed_kernel<DT, D, 2, true>), grid, block, 0, st, a);
+                else hipLaunchKernelGGL((ps_mixed_kernel<DT, D, 2, false>), grid, block, 0, st, a);
+            } else {
+                if (a.stream_kv) hipLaunchKernelGGL((ps_mixed_kernel<DT, D, 1, true>), grid, block, 0, st, a);
+                else hipLaunchKernelGGL((ps_mixed_kernel<DT, D, 1, false>), grid, block, 0, st, a);
+            }
             if (a.n_merge > 0)
                 hipLaunchKernelGGL((ps_merge_kernel<DT, D>), dim3(a.n_merge), dim3(256), 0, st, a);
             return hipGetLastError();
         }
     }
     if (a.n_decode > 0) {
-        if (a.decode_row_tiles == 2) {
-            hipLaunchKernelGGL((ps_decode_kernel<DT, D, 2, 4>), dim3(a.n_decode), dim3(256), 0, st, a);
-        } else if (a.decode_waves >= 16 && D == 64 && DT::ELT == 2) {
-            if constexpr (D == 64 && DT::ELT == 2)  // 16 waves fit the register budget only here
-                hipLaunchKernelGGL((ps_decode_kernel<DT, D, 1, 16>), dim3(a.n_decode), dim3(1024), 0, st, a);
-        } else if (a.decode_waves >= 8) {
-            hipLaunchKernelGGL((ps_decode_kernel<DT, D, 1, 8>), dim3(a.n_decode), dim3(512), 0, st, a);
-        } else {
-            hipLaunchKernelGGL((ps_decode_kernel<DT, D, 1, 4>), dim3(a.n_decode), dim3(256), 0, st, a);
-        }
+        auto decode = [&](auto streamc) {
+            constexpr bool STREAM = decltype(streamc)::value;
+            if (a.decode_row_tiles == 2) {
+                hipLaunchKernelGGL((ps_decode_kernel<DT, D, 2, 4, STREAM>), dim3(a.n_decode), dim3(256), 0, st, a);
+            } else if (a.decode_waves >= 16 && D == 64 && DT::ELT == 2) {
+                if constexpr (D == 64 && DT::ELT == 2)  // 16 waves fit the register budget only here
+                    hipLaunchKernelGGL((ps_decode_kernel<DT, D, 1, 16, STREAM>), dim3(a.n_decode), dim3(1024), 0, st, a);
+            } else if (a.decode_waves >= 8) {
+                hipLaunchKernelGGL((ps_decode_kernel<DT, D, 1, 8, STREAM>), dim3(a.n_decode), dim3(512), 0, st, a);
+            } else {
+                hipLaunchKernelGGL((ps_decode_kernel<DT, D, 1, 4, STREAM>), dim3(a.n_decode), dim3(256), 0, st, a);
+            }
+        };
+        if (a.stream_kv) decode(std::true_type{});
+        else decode(std::false_type{});
     }
     if (a.n_prefill > 0) {
         const dim3 grid(a.n_prefill), block(256);

@@ -28,6 +28,7 @@ struct ps_plan {
     uint32_t flags = 0;
     int32_t dec_rt = 1, dec_waves = 4;
     bool mixed = false, fixed = false;
+    bool stream_kv = false;   // decode K/V loads non-temporal
     int64_t ws_rows = 0;                 // workspace layout rows (fixed shape: the capacity)
     int32_t rows_cap = 0;                // packed tokens q / out hold (fixed shape: max_tokens)
     int32_t n_dec = 0, n_pre = 0, n_mrg = 0;   // launched items (fixed shape: capacities)
@@ -159,8 +160,10 @@ ps_status check_options(const ps_plan_options &o, uint32_t flags, const ps_pool 
     if (o.prefix_min_seqs < 0 || o.prefix_min_seqs == 1 || o.prefix_min_keys < 0 ||
         (o.prefix_min_keys > 0 && o.prefix_min_keys < PS_BLOCK))
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "prefix_min_seqs must be 0 or >= 2, prefix_min_keys 0 or >= 16");
-    for (int i = 0; i < 3; ++i)
+    for (int i = 0; i < 2; ++i)
         if (o.reserved[i] != 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "reserved option fields must be 0");
+    if (o.decode_stream_kv < 0 || o.decode_stream_kv > 2)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "decode_stream_kv %d: 0, 1 or 2", o.decode_stream_kv);
     if (o.decode_walk_rotation != 0 && o.decode_walk_rotation != 1)
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "decode_walk_rotation %d: 0 or 1", o.decode_walk_rotation);
     if (flags & PS_PLAN_FIXED_SHAPE) {
@@ -263,6 +266,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         return ps_fail(PS_ERR_HOST_MEMORY, "host allocation failed");
     }
     int64_t kv_rows_unique = 0;   // distinct (physical block, token) rows the step reads
+    int64_t shared_refs = 0;      // table entries naming a block an earlier table named
     {
         // clears every mark the step's entries may have set (also after an
         // error part way through)
@@ -286,7 +290,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         // one pass over every table entry the step covers, branch-free but
         // for the (rare) errors; `slot` gives the mark of a block id
         auto scan = [&](auto slot, auto prefetch) -> ps_status {
-            int64_t uniq = 0;
+            int64_t uniq = 0, again = 0;
             for (int32_t s = 0; s < S; ++s) {
                 const int32_t *row = block_tables + (int64_t)s * block_table_stride;
                 const int64_t ctx = (int64_t)num_computed_tokens[s] + q_lens[s];
@@ -309,10 +313,12 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                     const uint32_t old = m0 & 31u;
                     const uint32_t seen = m0 != 0u;
                     uniq += ntok > old ? ntok - old : 0;
+                    again += seen;
                     m = tag | (seen << 5) | std::max(ntok, old);
                 }
             }
             kv_rows_unique = uniq;
+            shared_refs = again;
             return PS_OK;
         };
         uint32_t *const dense = bm.dense.data();
@@ -643,6 +649,22 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         p->dec_waves = opt.decode_waves ? opt.decode_waves : (p->n_dec < 512 ? 8 : 4);
         if (dec_rt == 2 || p->mixed || p->dtype == PS_F32 || D != 64) p->dec_waves = std::min(p->dec_waves, 8);
         if (dec_rt == 2 || p->mixed) p->dec_waves = 4;
+        // Cache policy of the decode K/V loads. A step reads each
+        // unshared block once; when its decode K/V also exceed the 256 MiB
+        // last-level cache, caching them only evicts other data, and
+        // non-temporal loads ran 10% faster on MI355X (long-context verify,
+        // 1 GiB of K/V). Shared blocks are read again by other sequences in
+        // the same step, and smaller steps can still find their K/V cached
+        // from the step before: those keep the cached loads. A fixed-shape
+        // plan must not change kernels from step to step: cached.
+        {
+            int64_t dec_kv = 0;
+            for (int32_t s = 0; s < S; ++s)
+                if (is_dec[s])
+                    dec_kv += ((int64_t)num_computed_tokens[s] + q_lens[s]) * Hkv * 2 * D * elt_bytes(pool->dtype);
+            p->stream_kv = opt.decode_stream_kv == 1 ||
+                           (opt.decode_stream_kv == 0 && !fixed && shared_refs == 0 && dec_kv > ((int64_t)256 << 20));
+        }
 
         // ---- blob layout
         size_t off = 0;
@@ -730,6 +752,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         I.decode_waves = p->dec_waves;
         I.mixed_launch = p->mixed;
         I.decode_walk_rotation = opt.decode_walk_rotation;
+        I.decode_stream_kv = p->stream_kv ? 1 : 0;
         I.active_decode_items = act_dec;
         I.active_merge_items = act_mrg;
         I.workspace_rows = cap_ws;
@@ -901,6 +924,7 @@ static ps_status prepare_attention(const void *q, const ps_pool *pool, const int
     a.decode_row_tiles = plan->dec_rt;
     a.decode_waves = plan->dec_waves;
     a.mixed = plan->mixed;
+    a.stream_kv = plan->stream_kv ? 1 : 0;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.g = plan->Hq / plan->Hkv;
     ps_group_divisor(a.g, &a.g_magic, &a.g_shift);

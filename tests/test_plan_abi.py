@@ -328,6 +328,40 @@ def test_options_are_validated_and_recorded(monkeypatch):
         assert again[key] == dflt[key], key
 
 
+def test_decode_stream_choice():
+    """Decode K/V loads stream (non-temporal) only for steps that read every
+    block once and more decode K/V than the 256 MiB last-level cache; the
+    option forces either policy, and fixed-shape plans keep cached loads."""
+    INV = B.PS_ERR_INVALID_ARGUMENT
+    c3, c4, c5 = (workloads.config(i, values=False) for i in (3, 4, 5))
+    _expect_error(INV, _plan, c3, decode_stream_kv=3)
+    _expect_error(INV, _plan, c3, decode_stream_kv=-1)
+    info5 = P.ps_plan_get_info(_plan(c5))
+    assert info5["kv_bytes_decode"] > (256 << 20) and info5["kv_bytes_unique"] == (
+        info5["kv_bytes_decode"] + info5["kv_bytes_prefill"])
+    assert info5["decode_stream_kv"] == 1
+    # small step (its K/V fit the cache): cached
+    assert P.ps_plan_get_info(_plan(c3))["kv_bytes_decode"] < (256 << 20)
+    assert P.ps_plan_get_info(_plan(c3))["decode_stream_kv"] == 0
+    # shared prefix blocks are read again within the step: cached
+    assert P.ps_plan_get_info(_plan(c4))["kv_bytes_unique"] < P.ps_plan_get_info(_plan(c4))["kv_bytes_decode"]
+    assert P.ps_plan_get_info(_plan(c4))["decode_stream_kv"] == 0
+    # forced either way
+    assert P.ps_plan_get_info(_plan(c3, decode_stream_kv=1))["decode_stream_kv"] == 1
+    assert P.ps_plan_get_info(_plan(c5, decode_stream_kv=2))["decode_stream_kv"] == 0
+    # the choice changes nothing else in the plan
+    a, b = P.ps_plan_get_info(_plan(c5)), P.ps_plan_get_info(_plan(c5, decode_stream_kv=2))
+    for key in ("decode_items", "prefill_items", "merge_items", "decode_split_keys", "prefill_split_keys",
+                "decode_waves", "mixed_launch", "workspace_rows"):
+        assert a[key] == b[key], key
+    # a long unshared decode step in a fixed shape stays cached
+    long_ctx = workloads.build_step("fixed-long", 1, "bf16", 12, 2, 128, 80000, [1] * 32, [32767] * 32,
+                                    values=False)
+    fx = P.ps_plan_get_info(_plan(long_ctx, P.PS_PLAN_FIXED_SHAPE, max_seqs=32, max_tokens=32, max_query_len=1,
+                                  max_decode_items=1024, max_merge_items=4096, max_workspace_rows=1 << 16))
+    assert fx["kv_bytes_decode"] > (256 << 20) and fx["decode_stream_kv"] == 0
+
+
 def test_sequence_kernels():
     st = workloads.config(3, values=False)
     kinds = P.ps_plan_sequence_kernels(_plan(st), st.num_seqs)
