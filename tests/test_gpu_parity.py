@@ -352,6 +352,29 @@ def test_streamed_decode_loads_are_bit_identical(case):
         check_out(st, o1)
 
 
+@pytest.mark.parametrize("case", [("bf16", 12, 2, 128), ("f16", 14, 2, 64)], ids=["bf16-128", "f16-64"])
+def test_long_contexts_at_the_limits(case):
+    # contexts well past C5's: a decode row at 131072 keys, 5 verify rows at
+    # 65536 keys and a 200-token chunk at position 100000. The planner cuts
+    # them into dozens of key slices per row (the merge then takes its loop
+    # over more than 8 splits); every row against the oracle (~20 s on the
+    # host), the pool bit-exact
+    dt, hq, hkv, d = case
+    q_lens, nc = [1, 5, 200], [131071, 65531, 100000]
+    nb = sum((c + n + 15) // 16 for c, n in zip(nc, q_lens)) + 64
+    st = workloads.build_step(f"long-limits-{dt}-{d}", 77 + d, dt, hq, hkv, d, nb, q_lens, nc)
+    proto = P.ps_pool(0, 0, st.num_layers, st.num_blocks, 16, st.num_kv_heads, st.head_dim,
+                      P._binding.dtype_code(st.dtype), st.layer)
+    info = P.ps_plan_get_info(P.ps_plan_step(st.q_lens, st.num_computed, st.block_tables, st.num_q_heads, proto))
+    _note(f"{st.name}: {info['decode_items']} decode, {info['prefill_items']} prefill, {info['merge_items']} merges, "
+          f"decode split {info['decode_split_keys']}, prefill split {info['prefill_split_keys']}")
+    assert info["decode_split_keys"] <= 16384 and info["merge_items"] > 0
+    pools = H.host_pools(st)
+    out, gk, gv = run_on_gpu(st, pools=pools)
+    check_pool(st, pools, gk, gv)
+    check_out(st, out)
+
+
 def test_large_logits_stay_finite():
     st = workloads.random_step(17, dtype="bf16", num_q_heads=12, num_kv_heads=2, head_dim=128,
                                num_seqs=6, max_q=60, max_ctx=300)
