@@ -96,3 +96,30 @@ def test_config4_groups_whole_batch():
     out, gk, gv = run_on_gpu(st, SP, pools=pools)
     check_pool(st, pools, gk, gv)
     check_out(st, out)
+
+
+def test_long_prefix_slices_capped_at_the_item_limit():
+    # 61 sequences of 4 verify rows (64 query / 8 KV heads, head_dim 64)
+    # behind a 20480-token prefix: with the pass on, the group's 128
+    # (KV head, 128-row chunk) pairs would each take one prefix slice by
+    # the item-count rule, more keys than a prefill item stages block ids
+    # for (16384); the planner cuts every one in two. Every row against
+    # the oracle (~10 GB of host memory and ~20 s for the oracle's
+    # contiguous K/V).
+    S, prefix = 61, 20480
+    rng = np.random.default_rng(31)
+    nc = (prefix + rng.integers(1, 200, size=S, endpoint=True)).astype(np.int32)
+    st = workloads.build_step("long-prefix", 31, "bf16", 64, 8, 64, 4096, [4] * S, nc.tolist(),
+                              prefix_tokens=prefix)
+    info = _info(st)
+    _note(f"{st.summary()} groups={info['prefix_groups']} prefix_items={info['prefix_items']}")
+    assert info["prefix_groups"] == 1 and info["prefix_items"] == 2 * 8 * ceil_div(S * 4 * 8, 128)
+    pools = H.host_pools(st)
+    out, gk, gv = run_on_gpu(st, SP, pools=pools)
+    check_pool(st, pools, gk, gv)
+    del pools, gk, gv
+    check_out(st, out)
+
+
+def ceil_div(a, b):
+    return -(-a // b)
