@@ -20,8 +20,9 @@ struct ps_item {
     int32_t partial_row; // -1: write the output; else first workspace row of this item's partials
     int32_t flags;       // PS_ITEM_* bits
     // Decode items walk their 32-key tiles starting at tile `rot` (mod the
-    // tile count): items that share prefix blocks then do not request the
-    // same lines at the same time (softmax order is free). Prefill: 0.
+    // tile count); nonzero only with the walk-rotation plan option, where
+    // items that share prefix blocks then do not request the same lines at
+    // the same time (softmax order is free). Prefill: 0.
     int32_t rot;
     // Gathered items (PS_ITEM_GATHERED): which slice of the shared prefix's
     // keys the item covers; its partials go to a row's dest + split * stride.

@@ -683,7 +683,8 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     using FromTable = std::false_type;
     using FromLds = std::true_type;
     const int ntiles = (ke - kb + PS_DEC_TILE - 1) / PS_DEC_TILE;
-    // Items start their walk over the key range at different tiles, so that
+    // With the walk-rotation plan option an item starts its walk over the
+    // key range at an item-dependent tile (it.rot, 0 otherwise), so that
     // items sharing prefix blocks do not all ask for the same lines at once
     // (softmax order is free; the order is a fixed function of the item).
     const int rot = it.rot;
@@ -910,11 +911,11 @@ __global__ __launch_bounds__(64 * NW, NW >= 16 ? 4 : 2) void ps_decode_kernel(co
 // 16-bit data, 32 for fp32) are gathered through the block table straight
 // into LDS with global_load_lds_dwordx4 (no register staging) into a
 // two-stage ring, so the next tile streams in while the current one is
-// consumed. 16-byte chunks of each key row are XOR-swizzled by the row's
-// low 3 bits, which keeps the per-key K fragment reads and the per-row V
-// reads bank-conflict free without padding (the DMA writes whole 1 KiB
-// lines). Hand-offs use a bare s_barrier with explicit s_waitcnt, since a
-// fenced barrier would also wait for the tile still in flight.
+// consumed. 16-byte chunks of each key row are XOR-swizzled by the row
+// (swz), which keeps the per-key K fragment reads and the transposing V
+// reads off each other's LDS banks without padding (the DMA writes whole
+// 1 KiB lines). Hand-offs use a bare s_barrier with explicit s_waitcnt,
+// since a fenced barrier would also wait for the tile still in flight.
 
 
 // 4 16-bit values per lane, transposed within each 16-lane group: lane i

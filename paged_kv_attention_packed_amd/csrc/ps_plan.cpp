@@ -57,7 +57,8 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 // Split [0, kmax) into near-equal pieces of at most `target` keys, each a
 // multiple of `align` long except possibly the last (target a multiple of
 // align). The split set depends only on logical lengths, so physical
-// placement never changes results.
+// placement never changes results (only PS_PLAN_SHARED_PREFIX, which
+// groups sequences by the blocks they share, makes the work depend on it).
 void key_splits(int64_t kmax, int64_t target, int64_t align, std::vector<int64_t> &bounds) {
     bounds.clear();
     int64_t n = std::max<int64_t>(1, ceil_div(kmax, target));
