@@ -119,6 +119,9 @@ def test_config_parity_forced_path(idx, flags):
 CASES = [  # dtype, Hq, Hkv, D
     ("f32", 2, 1, 64), ("f32", 4, 2, 128), ("f16", 14, 2, 64), ("f16", 12, 2, 128),
     ("bf16", 12, 2, 128), ("bf16", 8, 8, 64), ("f16", 7, 1, 128), ("bf16", 32, 4, 64),
+    # one token already fills one (g = 16) or two (g = 32) 16-row tiles of a
+    # decode item; two tokens take the prefill kernel
+    ("f16", 16, 1, 64), ("bf16", 32, 1, 128),
 ]
 
 
