@@ -425,8 +425,10 @@ struct DecodeLds {
 };
 
 // STREAM: the item's K/V loads from the pool are non-temporal (the planner's
-// choice for steps that read each block once and more than the caches hold)
-template <class DT, int D, int RT, int NW, bool STREAM>
+// choice for steps that read each block once and more than the caches hold).
+// FUSE: the launch may carry the fused scatter (a.fuse_scatter); without it
+// the scatter's code and registers are compiled out.
+template <class DT, int D, int RT, int NW, bool STREAM, bool FUSE = true>
 __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, DecodeLds<DT, D, RT, NW> &sh) {
     using G = Geo<DT, D>;
     using T = typename DT::T;
@@ -466,7 +468,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     const int kb = it.key_begin, ke = it.key_end;
     // fused scatter: this step's keys (positions nc..) come from the inputs,
     // key position p from packed token qs0 + p - nc
-    const bool fused = a.fuse_scatter != 0;
+    const bool fused = FUSE && a.fuse_scatter != 0;
     const T *kn = static_cast<const T *>(fused ? a.k_new : a.pool_k) + (int64_t)j * D;
     const T *vn = static_cast<const T *>(fused ? a.v_new : a.pool_v) + (int64_t)j * D;
     const int new_lo = fused ? nc : INT32_MAX;   // keys in [new_lo, ke) are read from kn / vn
@@ -1397,7 +1399,7 @@ __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_laun
 // every round of resident items keeps some HBM reads running under the
 // MFMA work, instead of all of them running in the first rounds (C5 -1%;
 // with fewer prefill items it is slower: C3 +2%, C4 +17%).
-template <class DT, int D, int RT, bool STREAM>
+template <class DT, int D, int RT, bool STREAM, bool FUSE>
 __global__ __launch_bounds__(256, 2) void ps_mixed_kernel(const ps_attn_launch a) {
     __shared__ union {
         DecodeLds<DT, D, RT, 4> d;
@@ -1423,7 +1425,7 @@ __global__ __launch_bounds__(256, 2) void ps_mixed_kernel(const ps_attn_launch a
         dec = b < 2 * m ? (b & 1) == 0 : nd > np;
         idx = b < 2 * m ? b >> 1 : m + (b - 2 * m);
     }
-    if (dec) decode_item<DT, D, RT, 4, STREAM>(a, idx, L.d);
+    if (dec) decode_item<DT, D, RT, 4, STREAM, FUSE>(a, idx, L.d);
     else prefill_item<DT, D, PS_PRE_TILE, 2, 32>(a, idx, L.p);
 }
 
@@ -1505,13 +1507,24 @@ hipError_t launch_attention_t(const ps_attn_launch &a, hipStream_t st) {
     if constexpr (DT::ELT == 2) {
         if (a.n_decode > 0 && a.n_prefill > 0 && a.mixed) {
             const dim3 grid(a.n_decode + a.n_prefill), block(256);
-            if (a.decode_row_tiles == 2) {
-                if (a.stream_kv) hipLaunchKernelGGL((ps_mixed_kernel<DT, D, 2, true>), grid, block, 0, st, a);
-                else hipLaunchKernelGGL((ps_mixed_kernel<DT, D, 2, false>), grid, block, 0, st, a);
-            } else {
-                if (a.stream_kv) hipLaunchKernelGGL((ps_mixed_kernel<DT, D, 1, true>), grid, block, 0, st, a);
-                else hipLaunchKernelGGL((ps_mixed_kernel<DT, D, 1, false>), grid, block, 0, st, a);
-            }
+            // (a mixed launch fuses the scatter only next to shared-prefix
+            // items, so most mixed launches take the variant without it)
+            auto mixed = [&](auto rtc, auto streamc, auto fusec) {
+                hipLaunchKernelGGL((ps_mixed_kernel<DT, D, decltype(rtc)::value, decltype(streamc)::value,
+                                                    decltype(fusec)::value>), grid, block, 0, st, a);
+            };
+            using R1 = std::integral_constant<int, 1>;
+            using R2 = std::integral_constant<int, 2>;
+            auto by_fuse = [&](auto rtc, auto streamc) {
+                if (a.fuse_scatter) mixed(rtc, streamc, std::true_type{});
+                else mixed(rtc, streamc, std::false_type{});
+            };
+            auto by_stream = [&](auto rtc) {
+                if (a.stream_kv) by_fuse(rtc, std::true_type{});
+                else by_fuse(rtc, std::false_type{});
+            };
+            if (a.decode_row_tiles == 2) by_stream(R2{});
+            else by_stream(R1{});
             if (a.n_merge > 0)
                 hipLaunchKernelGGL((ps_merge_kernel<DT, D>), dim3(a.n_merge), dim3(256), 0, st, a);
             return hipGetLastError();
