@@ -378,6 +378,30 @@ def test_long_contexts_at_the_limits(case):
     check_out(st, out)
 
 
+@pytest.mark.parametrize("waves", [4, 8, 16])
+def test_decode_waves_options(waves):
+    # every waves-per-workgroup choice the options allow (16 only for
+    # head_dim 64 16-bit steps of one row tile) against the oracle, with the
+    # scatter fused (ps_step) and without
+    cases = [workloads.config(2)]
+    if waves != 16:
+        cases.append(workloads.build_step(f"decode-waves-{waves}", 40 + waves, "bf16", 12, 2, 128, 2048,
+                                          [1, 1, 1, 1, 1, 1], [17, 300, 1023, 1500, 64, 777]))
+    for st in cases:
+        info = P.ps_plan_get_info(P.ps_plan_step(
+            st.q_lens, st.num_computed, st.block_tables, st.num_q_heads,
+            P.ps_pool(0, 0, st.num_layers, st.num_blocks, 16, st.num_kv_heads, st.head_dim,
+                      P._binding.dtype_code(st.dtype), st.layer),
+            0, P.plan_options(decode_waves=waves)))
+        assert info["decode_waves"] == waves
+        _note(f"{st.name} decode_waves={waves}")
+        for separate in (False, True):
+            pools = H.host_pools(st)
+            out, gk, gv = run_on_gpu(st, pools=pools, separate=separate, decode_waves=waves)
+            check_pool(st, pools, gk, gv)
+            check_out(st, out)
+
+
 def test_large_logits_stay_finite():
     st = workloads.random_step(17, dtype="bf16", num_q_heads=12, num_kv_heads=2, head_dim=128,
                                num_seqs=6, max_q=60, max_ctx=300)
