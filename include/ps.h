@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PS_ABI_VERSION 4
+#define PS_ABI_VERSION 5
 
 typedef int32_t ps_status;
 enum {
@@ -150,10 +150,12 @@ typedef struct {
     int32_t max_decode_items;    /* 0 = max_seqs * num_kv_heads */
     int32_t max_merge_items;     /* 0: no key splits allowed */
     int32_t max_workspace_rows;  /* split-K partial rows (0 with no splits) */
-    int32_t decode_walk_rotation; /* 1: each decode item starts its walk over its key tiles at an
+    int32_t decode_walk_rotation; /* each decode item starts its walk over its key tiles at an
                                     item-dependent tile (helps when many items read the same
-                                    shared blocks); 0 (default): at its first tile. A function of
-                                    the item only, never of physical sharing */
+                                    shared blocks): 0 = planner's choice (on from 512 decode
+                                    items up, off for PS_PLAN_FIXED_SHAPE), 1 = on, 2 = off.
+                                    A function of the item and the step's logical shape, never
+                                    of physical sharing; it changes the summation order */
     int32_t decode_stream_kv;    /* cache policy of the decode kernel's K/V loads: 0 = planner's
                                     choice, 1 = non-temporal (streamed), 2 = cached. Results are the
                                     same either way; the planner streams when no physical block is
@@ -261,7 +263,7 @@ typedef struct {
     /* the choices the planner made (options resolved) */
     int32_t decode_split_keys, prefill_split_keys, decode_waves, mixed_launch;
     int32_t active_decode_items, active_merge_items;  /* items that do work (fixed shape pads) */
-    int32_t decode_walk_rotation;
+    int32_t decode_walk_rotation;               /* 1: decode items rotate their walks */
     int32_t decode_stream_kv;                   /* 1: decode K/V loads are non-temporal */
     int64_t workspace_rows;                     /* split-K partial rows */
     double plan_us;                             /* host time ps_plan_step took */

@@ -29,6 +29,7 @@ struct ps_plan {
     int32_t dec_rt = 1, dec_waves = 4;
     bool mixed = false, fixed = false;
     bool stream_kv = false;   // decode K/V loads non-temporal
+    bool rotate = false;      // decode walk rotation
     int64_t ws_rows = 0;                 // workspace layout rows (fixed shape: the capacity)
     int32_t rows_cap = 0;                // packed tokens q / out hold (fixed shape: max_tokens)
     int32_t n_dec = 0, n_pre = 0, n_mrg = 0;   // launched items (fixed shape: capacities)
@@ -165,8 +166,8 @@ ps_status check_options(const ps_plan_options &o, uint32_t flags, const ps_pool 
         if (o.reserved[i] != 0) return ps_fail(PS_ERR_INVALID_ARGUMENT, "reserved option fields must be 0");
     if (o.decode_stream_kv < 0 || o.decode_stream_kv > 2)
         return ps_fail(PS_ERR_INVALID_ARGUMENT, "decode_stream_kv %d: 0, 1 or 2", o.decode_stream_kv);
-    if (o.decode_walk_rotation != 0 && o.decode_walk_rotation != 1)
-        return ps_fail(PS_ERR_INVALID_ARGUMENT, "decode_walk_rotation %d: 0 or 1", o.decode_walk_rotation);
+    if (o.decode_walk_rotation < 0 || o.decode_walk_rotation > 2)
+        return ps_fail(PS_ERR_INVALID_ARGUMENT, "decode_walk_rotation %d: 0, 1 or 2", o.decode_walk_rotation);
     if (flags & PS_PLAN_FIXED_SHAPE) {
         if ((flags & 3) == PS_PLAN_ALL_PREFILL || (flags & PS_PLAN_SHARED_PREFIX))
             return ps_fail(PS_ERR_INVALID_ARGUMENT,
@@ -526,15 +527,6 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                         it.key_end = (int32_t)bounds[i + 1];
                         it.partial_row = nsplit > 1 ? (int32_t)(base + (npk + i) * (r1 - r0)) : -1;
                         it.flags = r1 == rows && i == ns - 1 ? PS_ITEM_WRITES_NEW : 0;
-                        if (d && opt.decode_walk_rotation) {
-                            // walks start at an item-dependent tile, so that
-                            // items reading the same blocks do not all ask for
-                            // the same lines at once (measured on MI355X:
-                            // 256 sequences behind one shared prefix -4%,
-                            // 64 short unshared decodes +16%: off by default)
-                            const int64_t ntiles = ceil_div(it.key_end - it.key_begin, PS_DEC_TILE);
-                            it.rot = ntiles > 1 ? (int32_t)((dec.size() * 13) % (size_t)ntiles) : 0;
-                        }
                         (d ? dec : pre).push_back(it);
                     }
                     if (nsplit > 1) {
@@ -598,6 +590,21 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                 delete p;
                 return ps_fail(PS_ERR_UNSUPPORTED, "prefill item of %d keys (internal limit %d)",
                                it.key_end - it.key_begin, PS_PRE_MAX_KEYS);
+            }
+        // Walk rotation: a decode item starts its walk at a tile that depends
+        // on the item's creation index, so that items reading the same
+        // blocks do not all ask for the same lines at once. It depends on
+        // the step's logical shape only, never on which blocks are shared.
+        // Measured on MI355X: 256 sequences behind one shared prefix (512
+        // items) -5%, the long-context verify step and the 1.5B mixed step
+        // unchanged, 64 short decodes (128 items) +16%; so by default on
+        // from 512 decode items (the resident workgroup slots) up.
+        p->rotate = opt.decode_walk_rotation == 1 ||
+                    (opt.decode_walk_rotation == 0 && !fixed && dec.size() >= 512);
+        if (p->rotate)
+            for (size_t k = 0; k < dec.size(); ++k) {
+                const int64_t ntiles = ceil_div(dec[k].key_end - dec[k].key_begin, PS_DEC_TILE);
+                dec[k].rot = ntiles > 1 ? (int32_t)((k * 13) % (size_t)ntiles) : 0;
             }
         // Longest decode items first (longest-processing-time order): in a
         // launch with more items than resident workgroups the ones that
@@ -752,7 +759,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         I.prefill_split_keys = (int32_t)pre_split;
         I.decode_waves = p->dec_waves;
         I.mixed_launch = p->mixed;
-        I.decode_walk_rotation = opt.decode_walk_rotation;
+        I.decode_walk_rotation = p->rotate ? 1 : 0;
         I.decode_stream_kv = p->stream_kv ? 1 : 0;
         I.active_decode_items = act_dec;
         I.active_merge_items = act_mrg;

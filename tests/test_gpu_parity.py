@@ -263,6 +263,22 @@ def test_prefix_sharing_is_bit_invariant():
     check_out(shared, osr)
     osp, _, _ = run_on_gpu(shared, P.PS_PLAN_SHARED_PREFIX)
     check_out(shared, osp)
+    # 256 sequences (512 decode items: the planner rotates walks by
+    # default): shared and private prefix blocks give the same bits
+    rng = np.random.default_rng(43)
+    nc = (256 + rng.integers(16, 400, size=256)).tolist()
+    big = workloads.build_step("shared-256", 43, "bf16", 12, 2, 128, 8192, [1] * 256, nc, prefix_tokens=256)
+    bigp = workloads.build_step("private-256", 44, "bf16", 12, 2, 128, 8192, big.q_lens, big.num_computed,
+                                values=False)
+    bigp.k_ctx, bigp.v_ctx = big.k_ctx, big.v_ctx
+    bigp.k, bigp.v, bigp.q = big.k, big.v, big.q
+    proto = P.ps_pool(0, 0, 1, big.num_blocks, 16, 2, 128, P.PS_BF16, 0)
+    info = P.ps_plan_get_info(P.ps_plan_step(big.q_lens, big.num_computed, big.block_tables, 12, proto))
+    assert info["decode_items"] >= 512 and info["decode_walk_rotation"] == 1
+    ob, _, _ = run_on_gpu(big)
+    obp, _, _ = run_on_gpu(bigp)
+    assert torch.equal(ob, obp), "512 items, rotated walks: sharing changed the output bits"
+    check_out(bigp, obp)
 
 
 def _caller_arrays(st, table=None):

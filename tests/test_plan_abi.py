@@ -362,6 +362,25 @@ def test_decode_stream_choice():
     assert fx["kv_bytes_decode"] > (256 << 20) and fx["decode_stream_kv"] == 0
 
 
+def test_walk_rotation_choice():
+    # walk rotation: the planner's choice is on from 512 decode items up
+    # (a function of the step's logical shape), off for fixed shapes; the
+    # option forces it either way
+    INV = B.PS_ERR_INVALID_ARGUMENT
+    c2, c4, c5 = (workloads.config(i, values=False) for i in (2, 4, 5))
+    _expect_error(INV, _plan, c2, decode_walk_rotation=3)
+    assert P.ps_plan_get_info(_plan(c2))["decode_walk_rotation"] == 0      # 128 items
+    assert P.ps_plan_get_info(_plan(c4))["decode_walk_rotation"] == 1      # 512 items
+    assert P.ps_plan_get_info(_plan(c5))["decode_walk_rotation"] == 1
+    assert P.ps_plan_get_info(_plan(c4, decode_walk_rotation=2))["decode_walk_rotation"] == 0
+    assert P.ps_plan_get_info(_plan(c2, decode_walk_rotation=1))["decode_walk_rotation"] == 1
+    # the same logical step with the prefix blocks shared or private: the
+    # same choice
+    priv = workloads.build_step("c4-private", 4, "bf16", 12, 2, 128, 32768, c4.q_lens.tolist(),
+                                c4.num_computed.tolist(), values=False)
+    assert P.ps_plan_get_info(_plan(priv))["decode_walk_rotation"] == 1
+
+
 def test_sequence_kernels():
     st = workloads.config(3, values=False)
     kinds = P.ps_plan_sequence_kernels(_plan(st), st.num_seqs)
