@@ -62,6 +62,11 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 // groups sequences by the blocks they share, makes the work depend on it).
 void key_splits(int64_t kmax, int64_t target, int64_t align, std::vector<int64_t> &bounds) {
     bounds.clear();
+    if (kmax <= target) {   // one slice (the common case, without the divisions)
+        bounds.push_back(0);
+        bounds.push_back(kmax);
+        return;
+    }
     int64_t n = std::max<int64_t>(1, ceil_div(kmax, target));
     int64_t len = round_up(ceil_div(kmax, n), align);
     n = ceil_div(kmax, len);
@@ -292,6 +297,9 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         // one pass over every table entry the step covers, branch-free but
         // for the (rare) errors; `slot` gives the mark of a block id
         auto scan = [&](auto slot, auto prefetch) -> ps_status {
+            // (a local copy: the marks' stores cannot alias it, so it stays
+            // in a register instead of being reloaded per entry)
+            const uint32_t nb = (uint32_t)NB;
             int64_t uniq = 0, again = 0;
             for (int32_t s = 0; s < S; ++s) {
                 const int32_t *row = block_tables + (int64_t)s * block_table_stride;
@@ -300,24 +308,38 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                 const uint32_t tag = (uint32_t)(s + 1) << 6;
                 constexpr int64_t kAhead = 16;
                 for (int64_t b = 0; b < std::min(nblk, kAhead); ++b) prefetch(row[b]);
-                for (int64_t b = 0; b < nblk; ++b) {
+                // blocks before the last are full (16 tokens, never fewer
+                // than a mark holds), the last holds the rest
+                const int64_t nfull = nblk - 1;
+                auto entry = [&](int64_t b, uint32_t ntok, auto full) -> bool {
                     const int32_t id = row[b];
-                    if ((uint32_t)id >= (uint32_t)NB)
-                        return ps_fail(PS_ERR_INVALID_ARGUMENT, "block_tables[%d][%lld] = %d outside [0, %d)", s,
-                                       (long long)b, id, NB);
+                    if ((uint32_t)id >= nb) {
+                        ps_fail(PS_ERR_INVALID_ARGUMENT, "block_tables[%d][%lld] = %d outside [0, %d)", s,
+                                (long long)b, id, NB);
+                        return false;
+                    }
                     if (b + kAhead < nblk) prefetch(row[b + kAhead]);
-                    const uint32_t ntok = (uint32_t)std::min<int64_t>(PS_BLOCK, ctx - b * PS_BLOCK);
                     uint32_t &m = slot(id);
                     const uint32_t m0 = m;
-                    if ((m0 >> 6) == (uint32_t)(s + 1))
-                        return ps_fail(PS_ERR_INVALID_ARGUMENT, "block %d appears twice in the table of sequence %d",
-                                       id, s);
+                    if ((m0 >> 6) == (uint32_t)(s + 1)) {
+                        ps_fail(PS_ERR_INVALID_ARGUMENT, "block %d appears twice in the table of sequence %d", id, s);
+                        return false;
+                    }
                     const uint32_t old = m0 & 31u;
                     const uint32_t seen = m0 != 0u;
-                    uniq += ntok > old ? ntok - old : 0;
                     again += seen;
-                    m = tag | (seen << 5) | std::max(ntok, old);
-                }
+                    if constexpr (decltype(full)::value) {
+                        uniq += PS_BLOCK - old;
+                        m = tag | (seen << 5) | PS_BLOCK;
+                    } else {
+                        uniq += ntok > old ? ntok - old : 0;
+                        m = tag | (seen << 5) | std::max(ntok, old);
+                    }
+                    return true;
+                };
+                for (int64_t b = 0; b < nfull; ++b)
+                    if (!entry(b, PS_BLOCK, std::true_type{})) return PS_ERR_INVALID_ARGUMENT;
+                if (!entry(nfull, (uint32_t)(ctx - nfull * PS_BLOCK), std::false_type{})) return PS_ERR_INVALID_ARGUMENT;
             }
             kv_rows_unique = uniq;
             shared_refs = again;
@@ -358,6 +380,7 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         // ---- work lists
         std::vector<ps_item> dec, pre;
         std::vector<ps_merge> mrg;
+        dec.reserve((size_t)S * Hkv);
         std::vector<char> is_dec(S);
         for (int32_t s = 0; s < S; ++s) {
             const int64_t rows = (int64_t)g * q_lens[s];
@@ -603,8 +626,8 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
                     (opt.decode_walk_rotation == 0 && !fixed && dec.size() >= 512);
         if (p->rotate)
             for (size_t k = 0; k < dec.size(); ++k) {
-                const int64_t ntiles = ceil_div(dec[k].key_end - dec[k].key_begin, PS_DEC_TILE);
-                dec[k].rot = ntiles > 1 ? (int32_t)((k * 13) % (size_t)ntiles) : 0;
+                const uint32_t ntiles = (uint32_t)ceil_div(dec[k].key_end - dec[k].key_begin, PS_DEC_TILE);
+                dec[k].rot = ntiles > 1 ? (int32_t)((uint32_t)(k * 13) % ntiles) : 0;
             }
         // Longest decode items first (longest-processing-time order): in a
         // launch with more items than resident workgroups the ones that
@@ -614,10 +637,17 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         // (C2, 128 items) gains nothing and keeps the sequence order.
         // Nothing else depends on the order: merges and partials are
         // addressed by workspace row.
-        if (!pre.empty() || dec.size() > 256)
-            std::stable_sort(dec.begin(), dec.end(), [](const ps_item &x, const ps_item &y) {
-                return x.key_end - x.key_begin > y.key_end - y.key_begin;
-            });
+        if (!pre.empty() || dec.size() > 256) {
+            // (a stable sort on 8-byte keys, the original index breaking
+            // ties, then one pass moving the items)
+            std::vector<uint64_t> order(dec.size());
+            for (size_t k = 0; k < dec.size(); ++k)
+                order[k] = (uint64_t)(uint32_t)(INT32_MAX - (dec[k].key_end - dec[k].key_begin)) << 32 | k;
+            std::sort(order.begin(), order.end());
+            std::vector<ps_item> sorted(dec.size());
+            for (size_t k = 0; k < dec.size(); ++k) sorted[k] = dec[(uint32_t)order[k]];
+            dec.swap(sorted);
+        }
 
         // ---- launch shape (fixed: from the capacities alone)
         const int32_t act_dec = (int32_t)dec.size(), act_mrg = (int32_t)mrg.size();
@@ -721,18 +751,25 @@ extern "C" ps_status ps_plan_step(const int32_t *q_lens, const int32_t *num_comp
         if (!rmap.empty()) std::memcpy(p->host<ps_row>(p->off_rmap), rmap.data(), sizeof(ps_row) * rmap.size());
         // decode items' first tiles in walk order: tile t covers keys
         // key_begin + 32 u .. +32, u = (t + rot) mod ntiles; a tile's second
-        // block past key_end repeats the first (never read)
+        // block past key_end repeats the first (never read). A wave of an
+        // item of NW waves takes its first tiles, t = wave and wave + NW,
+        // from here: entries from 2 NW on are never read and stay zero.
         int32_t *dh = p->host<int32_t>(p->off_dhead);
+        const int32_t head_tiles = std::min<int32_t>(PS_DEC_HEAD_TILES, 2 * p->dec_waves);
+        static_assert(PS_DEC_TILE == 2 * PS_BLOCK, "a decode tile spans two blocks");
         for (size_t i = 0; i < (size_t)act_dec; ++i) {
             const ps_item &it = dec[i];
-            const int32_t *row = block_tables + (int64_t)it.seq * block_table_stride;
-            const int32_t ntiles = (it.key_end - it.key_begin + PS_DEC_TILE - 1) / PS_DEC_TILE;
+            // (decode slices start on block boundaries)
+            const int32_t *blk = block_tables + (int64_t)it.seq * block_table_stride + it.key_begin / PS_BLOCK;
+            const int32_t len = it.key_end - it.key_begin;
+            const int32_t ntiles = (len + PS_DEC_TILE - 1) / PS_DEC_TILE;
+            const int32_t n = std::min<int32_t>(ntiles, head_tiles);
+            int32_t *d = dh + i * 2 * PS_DEC_HEAD_TILES;
             int32_t u = it.rot;
-            for (int32_t t = 0; t < std::min<int32_t>(ntiles, PS_DEC_HEAD_TILES); ++t) {
-                const int32_t k0 = it.key_begin + u * PS_DEC_TILE;
-                const int32_t b0 = row[k0 / PS_BLOCK];
-                dh[i * 2 * PS_DEC_HEAD_TILES + 2 * t] = b0;
-                dh[i * 2 * PS_DEC_HEAD_TILES + 2 * t + 1] = k0 + PS_BLOCK < it.key_end ? row[k0 / PS_BLOCK + 1] : b0;
+            for (int32_t t = 0; t < n; ++t) {
+                const int32_t b0 = blk[2 * u];
+                d[2 * t] = b0;
+                d[2 * t + 1] = PS_DEC_TILE * u + PS_BLOCK < len ? blk[2 * u + 1] : b0;
                 u = u + 1 == ntiles ? 0 : u + 1;
             }
         }
