@@ -107,11 +107,17 @@ __device__ inline void swap_pair32(float x, float &a, float &b) {
     a = __builtin_bit_cast(float, r0);
     b = __builtin_bit_cast(float, r1);
 }
+// (max(a, b) as the median of a, b and FLT_MAX: the same value unless an
+// operand is +inf or NaN, i.e. an overflowed score, whose softmax has no
+// finite value either way. fmaxf would first quiet its operands, two more
+// VALU ops each time, since the swap results come from integer
+// operations; the reduction runs for every row tile of every key tile.)
+__device__ inline float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, 3.4028234663852886e38f); }
 __device__ inline float xor_max(float x) {
     float a, b;
     swap_pair16(x, a, b);
-    swap_pair32(fmaxf(a, b), a, b);
-    return fmaxf(a, b);
+    swap_pair32(max2(a, b), a, b);
+    return max2(a, b);
 }
 __device__ inline float xor_sum(float x) {
     float a, b;
