@@ -122,6 +122,10 @@ def test_validation_errors():
     _expect_error(INV, P.ps_plan_step, [1, 1], [-1, 3], bt, 4, pool, match="num_computed")
     _expect_error(INV, P.ps_plan_step, [1, 1], [3, 40], bt, 4, pool, match="table width")
     _expect_error(INV, P.ps_plan_step, [1, 1], [3, 3], np.array([[0, 1], [9, 3]]), 4, pool, match="outside")
+    # (the same in a full block, which the scan takes on its own path, and
+    # a negative id)
+    _expect_error(INV, P.ps_plan_step, [1, 1], [20, 3], np.array([[9, 1], [2, 3]]), 4, pool, match="outside")
+    _expect_error(INV, P.ps_plan_step, [1, 1], [20, 3], np.array([[-1, 1], [2, 3]]), 4, pool, match="outside")
     _expect_error(INV, P.ps_plan_step, [1, 1], [3, 20], np.array([[0, 1], [2, 2]]), 4, pool, match="twice")
     # sequence 1 appends into block 0, which sequence 0 also reads
     _expect_error(INV, P.ps_plan_step, [1, 1], [20, 3], np.array([[0, 1], [0, 3]]), 4, pool, match="share")
