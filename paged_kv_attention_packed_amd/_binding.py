@@ -100,6 +100,12 @@ class PsError(RuntimeError):
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_attention_packed_amd.build`")
 
+# torch first: its HIP runtime (a copy of libamdhip64 that its own libraries
+# load by file name) is then the one libps.so binds to, by soname. Opened
+# the other way round, the process would hold two HIP runtimes, and the
+# library's calls would not see the device torch allocates on.
+import torch  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _vp = ctypes.c_void_p

@@ -37,6 +37,21 @@ def test_library_exports_every_declared_symbol():
     assert P.ps_abi_version() == int(re.search(r"#define PS_ABI_VERSION (\d+)", header).group(1))
 
 
+def test_one_hip_runtime_whatever_the_import_order():
+    # imported before torch, the package must still leave a single HIP
+    # runtime in the process (torch's), or the library's calls would not
+    # see the device torch allocates on
+    import subprocess
+    import sys
+    code = ("import paged_kv_attention_packed_amd, torch\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))\n")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.strip().splitlines()[-1] == "1", res.stdout
+
+
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
 def test_planner_arrays_match_oracle_slot_formula(idx):
     st = workloads.config(idx, values=False)
