@@ -204,10 +204,11 @@ class Plan:
 
     def __init__(self, handle: int):
         self.handle = handle
+        self._lib = lib   # (module globals may be gone when the last plans die at exit)
 
     def __del__(self):
-        if getattr(self, "handle", None):
-            lib.ps_plan_destroy(self.handle)
+        if getattr(self, "handle", None) and getattr(self, "_lib", None) is not None:
+            self._lib.ps_plan_destroy(self.handle)
             self.handle = None
 
 
