@@ -424,8 +424,11 @@ def test_large_logits_stay_finite():
     st.scale *= 30.0
     for flags in (P.PS_PLAN_ALL_DECODE, P.PS_PLAN_ALL_PREFILL):
         out, _, _ = run_on_gpu(st, flags=flags)
-        # with logits ~N(0, 30^2) the softmax is nearly one-hot, so bf16
-        # rounding of P shifts whole values: compare at the value scale
+        # with logits ~N(0, 30^2) the softmax is nearly one-hot: an output
+        # is close to a single V value (magnitude up to ~4), whose rounding
+        # to bf16 alone costs up to 0.0078 (0.0156 above 4), so the
+        # element-wise bound is the value scale's; the row-relative bound
+        # keeps the standard 1e-2 (measured 2.2e-3, 0.0101 absolute)
         check_out(st, out, tol=2e-2)
 
 
