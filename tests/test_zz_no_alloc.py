@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def _run(st, entry, options):
+def _run(st, entry, options, flags=P.PS_PLAN_DEFAULT):
     """One step through `entry` ("step": ps_step with a torch workspace;
     "no_alloc": ps_step_no_alloc) on a fresh device pool; returns
     (out, pool_k bits, pool_v bits, pools before, plan info)."""
@@ -29,7 +29,7 @@ def _run(st, entry, options):
     gk = torch.from_numpy(pools[0]).to(DEV).view(st.dtype)
     gv = torch.from_numpy(pools[1]).to(DEV).view(st.dtype)
     pool = P.make_pool(gk, gv, st.layer)
-    step = P.PackedStep(st.q_lens, st.num_computed, st.block_tables, st.num_q_heads, pool, DEV,
+    step = P.PackedStep(st.q_lens, st.num_computed, st.block_tables, st.num_q_heads, pool, DEV, flags,
                         options=P.plan_options(**options))
     q, k, v = st.q.to(DEV), st.k.to(DEV), st.v.to(DEV)
     out = torch.full_like(q, float("nan"))
@@ -80,3 +80,20 @@ def test_no_alloc_refuses_oversized_workspace():
         P.ps_step_no_alloc(1 << 22, 1 << 23, 1 << 24, 1 << 25, pool, 1 << 26, st.block_tables.shape[1],
                            1 << 27, 1 << 28, 1 << 29, 1 << 30, st.num_seqs, st.num_tokens, 12, 0.088, plan)
     assert e.value.status == B.PS_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_no_alloc_matches_step_on_sweep_cases():
+    # twelve of the seeded sweep's steps (routes, plan options, dtypes and
+    # head shapes drawn there), back to back on the same static array:
+    # ps_step's output bit for bit every time
+    from tests.test_gpu_sweep import _cases
+    for case in _cases()[::5]:
+        i, dt, d, hq, hkv, num_seqs, max_q, max_ctx, flags, opts, _ = case
+        st = workloads.random_step(7000 + i, dtype=dt, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                                   num_seqs=num_seqs, max_q=max_q, max_ctx=max_ctx)
+        print(f"[gpu-case] no-alloc sweep case {i}: {dt} Hq={hq} Hkv={hkv} D={d} flags={flags} opts={opts}",
+              flush=True)
+        ref, rk, rv, _, _ = _run(st, "step", opts, flags)
+        got, gk, gv, pools, _ = _run(st, "no_alloc", opts, flags)
+        assert torch.equal(got, ref), f"sweep case {i}: ps_step_no_alloc output differs from ps_step"
+        assert np.array_equal(gk, rk) and np.array_equal(gv, rv), f"sweep case {i}: pools differ"
