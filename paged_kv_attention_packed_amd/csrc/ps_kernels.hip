@@ -962,17 +962,16 @@ __device__ inline void lds_row_words(const uint8_t *rowp, int row, int off, uint
 
 // TK: keys per tile; OCC: waves per SIMD the register budget is sized for
 // (1: 512 registers, accumulators may live in AGPRs; 2: 256 registers)
-template <class DT, int D, int TK, int NST>
+template <class DT, int D, int TK>
 struct PrefillLds {
     static constexpr int STAGEB = 2 * TK * D * DT::ELT;  // one ring stage: K tile, then V tile
     __attribute__((aligned(1024))) uint8_t ring0[STAGEB];
     __attribute__((aligned(1024))) uint8_t ring1[STAGEB];
-    __attribute__((aligned(1024))) uint8_t ring2[NST == 3 ? STAGEB : 1024];
     int32_t bt[PS_PRE_MAX_KEYS / PS_BLOCK];  // the item's block ids
 };
 
-template <class DT, int D, int TK, int NST, int RPW>
-__device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, PrefillLds<DT, D, TK, NST> &sh) {
+template <class DT, int D, int TK, int RPW>
+__device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, PrefillLds<DT, D, TK> &sh) {
     using G = Geo<DT, D>;
     using T = typename DT::T;
     constexpr int ELT = G::ELT, KU4 = G::KU4, VW = G::VW, NT = G::NT, EPL = G::EPL;
@@ -986,15 +985,10 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
     static_assert(CPR >= 8 && TILEB % 4096 == 0, "tile geometry");
     static_assert(2 * RPW * D * ELT <= STAGEB, "output staging fits the ring");
 
-    static_assert(NST == 2 || NST == 3, "ring stages");
-    static_assert(PrefillLds<DT, D, TK, NST>::STAGEB == STAGEB, "stage size");
+    static_assert(PrefillLds<DT, D, TK>::STAGEB == STAGEB, "stage size");
     uint8_t *const ring0 = sh.ring0;
     uint8_t *const ring1 = sh.ring1;
-    uint8_t *const ring2 = sh.ring2;
-    auto stage = [&](auto sc) -> uint8_t * {
-        constexpr int st = decltype(sc)::value;
-        return st == 0 ? ring0 : st == 1 ? ring1 : ring2;
-    };
+    auto stage = [&](auto sc) -> uint8_t * { return decltype(sc)::value == 0 ? ring0 : ring1; };
     int32_t *const sbt = sh.bt;
 
     const ps_item it = a.prefill_items[item];
@@ -1084,7 +1078,6 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
 
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
     // Tile 0's DMA goes out first, with its block ids read straight from the
     // table (scalar loads), so that its latency overlaps the Q rows' and the
     // staged ids' instead of following them.
@@ -1273,18 +1266,18 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
         __builtin_amdgcn_s_setprio(0);
     };
 
-    // Tile ti sits in stage ti % NST; the NST - 1 tiles after it stream in
-    // while it is consumed. One barrier per tile: once every thread's
-    // loads of tile ti have landed, every wave has also finished tile
-    // ti - 1, so its stage takes tile ti + NST - 1.
+    // Tile ti sits in stage ti % 2; the tile after it streams in while it
+    // is consumed. One barrier per tile: once every thread's loads of tile
+    // ti have landed, every wave has also finished tile ti - 1, so its
+    // stage takes tile ti + 1.
     // Past the end a step re-reads its own tile instead of branching around
     // the issue: a branch here would make the compiler wait for the tiles
     // in flight before every LDS read.
     auto step = [&](auto cur, auto ahead, int ti, int ntiles) {
         const int k0 = kb + ti * TK;
-        const int kn = ti + NST - 1 < ntiles ? k0 + (NST - 1) * TK : k0;
+        const int kn = ti + 1 < ntiles ? k0 + TK : k0;
         const IdVec ids = read_ids(kn);
-        wait_vmcnt<(NST - 2) * NLD>();  // this thread's loads of tile ti have landed
+        wait_vmcnt<0>();                // this thread's loads of tile ti have landed
         lds_barrier();                  // ... and every other thread's
         issue_tile(ahead, kn, ids);
         if constexpr (ELT == 2) {
@@ -1302,21 +1295,9 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
         }
         if (active && k0 <= lim_hi) compute_tile(cur, k0);
     };
-    if (ntiles > 0) {
-        if constexpr (NST == 3) {
-            const int k1 = ntiles > 1 ? kb + TK : kb;
-            issue_tile(S1{}, k1, read_ids(k1));
-        }
-    }
-    for (int ti = 0; ti < ntiles; ti += NST) {
-        if constexpr (NST == 2) {
-            step(S0{}, S1{}, ti, ntiles);
-            if (ti + 1 < ntiles) step(S1{}, S0{}, ti + 1, ntiles);
-        } else {
-            step(S0{}, S2{}, ti, ntiles);
-            if (ti + 1 < ntiles) step(S1{}, S0{}, ti + 1, ntiles);
-            if (ti + 2 < ntiles) step(S2{}, S1{}, ti + 2, ntiles);
-        }
+    for (int ti = 0; ti < ntiles; ti += 2) {
+        step(S0{}, S1{}, ti, ntiles);
+        if (ti + 1 < ntiles) step(S1{}, S0{}, ti + 1, ntiles);
     }
 
     wait_vmcnt<0>();  // the last, unused tile must land before the ring is reused
@@ -1382,10 +1363,10 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
     }
 }
 
-template <class DT, int D, int TK, int OCC, int NST, int RPW>
+template <class DT, int D, int TK, int OCC, int RPW>
 __global__ __launch_bounds__(256, OCC) void ps_prefill_kernel(const ps_attn_launch a) {
-    __shared__ PrefillLds<DT, D, TK, NST> L;
-    prefill_item<DT, D, TK, NST, RPW>(a, blockIdx.x, L);
+    __shared__ PrefillLds<DT, D, TK> L;
+    prefill_item<DT, D, TK, RPW>(a, blockIdx.x, L);
 }
 
 // Decode and prefill items of one step in a single launch, so that the
@@ -1409,7 +1390,7 @@ template <class DT, int D, int RT, bool STREAM, bool FUSE>
 __global__ __launch_bounds__(256, 2) void ps_mixed_kernel(const ps_attn_launch a) {
     __shared__ union {
         DecodeLds<DT, D, RT, 4> d;
-        PrefillLds<DT, D, PS_PRE_TILE, 2> p;
+        PrefillLds<DT, D, PS_PRE_TILE> p;
     } L;
     const int nd = a.n_decode, np = a.n_prefill, m = min(nd, np);
     const int b = blockIdx.x;
@@ -1432,7 +1413,7 @@ __global__ __launch_bounds__(256, 2) void ps_mixed_kernel(const ps_attn_launch a
         idx = b < 2 * m ? b >> 1 : m + (b - 2 * m);
     }
     if (dec) decode_item<DT, D, RT, 4, STREAM, FUSE>(a, idx, L.d);
-    else prefill_item<DT, D, PS_PRE_TILE, 2, 32>(a, idx, L.p);
+    else prefill_item<DT, D, PS_PRE_TILE, 32>(a, idx, L.p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1556,9 +1537,9 @@ hipError_t launch_attention_t(const ps_attn_launch &a, hipStream_t st) {
     if (a.n_prefill > 0) {
         const dim3 grid(a.n_prefill), block(256);
         if constexpr (DT::ELT == 4)
-            hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 2, 32>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE / 2, 2, 32>), grid, block, 0, st, a);
         else
-            hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE, 2, 2, 32>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((ps_prefill_kernel<DT, D, PS_PRE_TILE, 2, 32>), grid, block, 0, st, a);
     }
     if (a.n_merge > 0)
         hipLaunchKernelGGL((ps_merge_kernel<DT, D>), dim3(a.n_merge), dim3(256), 0, st, a);
