@@ -852,13 +852,19 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     for (int i = 0; i < SPT; ++i) asm volatile("" ::"v"(stg[i]));
 
     // ---- merge the waves' states
+    // A wave's partial O goes to its LDS region lane-major: entry
+    // cb = (rt * 4 + i) * NT + t of every lane (row rt * 16 + c, column
+    // EPL * (4 q4 + i) + t) sits at cb * 64 + lane. Each store, and each
+    // read below, then covers 64 consecutive words: no bank conflicts
+    // (row-major, the 16 lanes of one column would all hit one bank).
+    constexpr int NE = RT * 4 * NT;   // entries per lane
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         l[rt] = xor_sum(l[rt]);
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sh.o[wave][rt * 16 + c][EPL * (4 * q4 + i) + t] = o[rt][t][i];
+            for (int t = 0; t < NT; ++t) (&sh.o[wave][0][0])[((rt * 4 + i) * NT + t) * 64 + lane] = o[rt][t][i];
         if (q4 == 0) {
             sh.m[wave][rt * 16 + c] = m[rt];
             sh.l[wave][rt * 16 + c] = l[rt];
@@ -866,10 +872,14 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
     }
     __syncthreads();
 
-    constexpr int EPT = ROWS * D / (64 * NW);  // output elements per thread (>= 1)
-    static_assert(EPT >= 1, "too many waves for the rows");
-    const int e0 = tid * EPT;
-    const int row = e0 / D, d0 = e0 % D;
+    // Thread (wave, lane) finishes entries [wave * EPT, wave * EPT + EPT)
+    // of the lane's position: one row tile rt0, columns d0 .. d0 + EPT - 1
+    // (EPL = NT, so column EPL * (4 q4 + i) + t is 4 NT q4 + cb mod 4 NT).
+    constexpr int EPT = NE / NW;   // output elements per thread (>= 1)
+    static_assert(EPT >= 1 && NE % NW == 0 && (4 * NT) % EPT == 0, "waves do not split the entries");
+    static_assert(EPL == NT && NE * 64 == ROWS * D, "entry layout");
+    const int cb0 = wave * EPT;
+    const int row = cb0 / (4 * NT) * 16 + c, d0 = 4 * NT * q4 + cb0 % (4 * NT);
     const int r = it.row_begin + row;
     if (r >= it.row_end) return;
     float mw[NW], M = kNegInf;
@@ -887,7 +897,7 @@ __device__ __forceinline__ void decode_item(const ps_attn_launch a, int item, De
         const float f = fast_exp2(mw[w] - muse);
         L += sh.l[w][row] * f;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) acc[e] += sh.o[w][row][d0 + e] * f;
+        for (int e = 0; e < EPT; ++e) acc[e] += (&sh.o[w][0][0])[(cb0 + e) * 64 + lane] * f;
     }
     if (it.partial_row < 0) {
         const int tok = div_g(a, r);
