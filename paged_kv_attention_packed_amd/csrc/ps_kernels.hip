@@ -1343,25 +1343,36 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
         return;
     }
 
-    // final output: normalise, round, transpose through LDS, write rows
-    T *so = reinterpret_cast<T *>(wave < 2 ? ring0 : ring1) + (wave & 1) * RPW * D;
+    // final output: normalise, round, transpose through LDS, write rows.
+    // Chunk ch (16 bytes) of staged row `row` sits at ch ^ (row mod OCPR):
+    // the 16 lanes that hold one column of a row tile then store to 16
+    // different chunks (unswizzled, a row is 256 bytes and all 16 would
+    // hit one bank).
+    constexpr int OCPR = D * ELT / 16;   // 16-byte chunks per output row
+    static_assert((OCPR & (OCPR - 1)) == 0, "chunks per row: a power of two");
+    uint8_t *const sob = (wave < 2 ? ring0 : ring1) + (wave & 1) * RPW * D * ELT;
+    auto staged = [&](int row, int byte) { return sob + row * (D * ELT) + (((byte >> 4) ^ (row & (OCPR - 1))) << 4) + (byte & 15); };
     if (active) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const float inv = l[rt] > 0.f ? 1.f / l[rt] : 0.f;
+            const int row = rt * 16 + c;
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT; ++t) {
+                if constexpr (ELT == 2) {   // d = 16t + 4q4 .. +3: one 8-byte store
+                    const u32x2 w = {pack2(o[rt][t][0] * inv, o[rt][t][1] * inv, DT{}),
+                                     pack2(o[rt][t][2] * inv, o[rt][t][3] * inv, DT{})};
+                    *reinterpret_cast<u32x2 *>(staged(row, (16 * t + 4 * q4) * ELT)) = w;
+                } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int d = ELT == 2 ? 16 * t + 4 * q4 + i : EPL * (4 * q4 + i) + t;
-                    so[(rt * 16 + c) * D + d] = cvt_out(o[rt][t][i] * inv, DT{});
+                    for (int i = 0; i < 4; ++i)
+                        *reinterpret_cast<T *>(staged(row, (EPL * (4 * q4 + i) + t) * ELT)) = cvt_out(o[rt][t][i] * inv, DT{});
                 }
+            }
         }
     }
     __syncthreads();
     if (!active) return;
-    constexpr int OCPR = D * ELT / 16;
-    const uint8_t *sob = reinterpret_cast<const uint8_t *>(so);
     for (int x = lane; x < RPW * OCPR; x += 64) {
         const int row = x / OCPR, ch = x - row * OCPR;
         const int r = wr0 + row;
@@ -1369,7 +1380,7 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
         const int tok = div_g(a, r);
         const int h = j * g + (r - tok * g);
         uint8_t *dst = static_cast<uint8_t *>(a.out) + (((int64_t)tok_index(a, qs0, tok) * a.num_q_heads + h) * D) * ELT;
-        reinterpret_cast<u32x4 *>(dst)[ch] = *reinterpret_cast<const u32x4 *>(sob + row * D * ELT + ch * 16);
+        reinterpret_cast<u32x4 *>(dst)[ch] = *reinterpret_cast<const u32x4 *>(staged(row, ch * 16));
     }
 }
 
