@@ -1433,8 +1433,15 @@ __global__ __launch_bounds__(256, 2) void ps_mixed_kernel(const ps_attn_launch a
         dec = b < 2 * m ? (b & 1) == 0 : nd > np;
         idx = b < 2 * m ? b >> 1 : m + (b - 2 * m);
     }
-    if (dec) decode_item<DT, D, RT, 4, STREAM, FUSE>(a, idx, L.d);
-    else prefill_item<DT, D, PS_PRE_TILE, 32>(a, idx, L.p);
+    if (dec) {
+        // Decode waves run at the prefill waves' MFMA level throughout,
+        // above their softmax phases: the few instructions between a decode
+        // wave's loads then issue promptly and keep its loads flowing.
+        __builtin_amdgcn_s_setprio(1);
+        decode_item<DT, D, RT, 4, STREAM, FUSE>(a, idx, L.d);
+    } else {
+        prefill_item<DT, D, PS_PRE_TILE, 32>(a, idx, L.p);
+    }
 }
 
 // ---------------------------------------------------------------------------
