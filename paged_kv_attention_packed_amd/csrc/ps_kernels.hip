@@ -1139,6 +1139,12 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
     wait_vmcnt<0>();
     __syncthreads();
 
+    // The all-ones A operand of the row-sum MFMAs, held in VGPRs for the
+    // whole item (the empty asm makes it opaque): as a constant, the
+    // compiler rebuilt it from SGPRs with two 64-bit moves at every use.
+    constexpr uint32_t one2 = std::is_same<DT, TBF16>::value ? 0x3F803F80u : 0x3C003C00u;
+    u32x4 ones = {one2, one2, one2, one2};
+    if constexpr (ELT == 2) asm volatile("" : "+v"(ones));
     auto compute_tile = [&](auto stagec, int k0) {
         const uint8_t *ksm = stage(stagec);
         const uint8_t *vsm = ksm + TILEB;
@@ -1228,8 +1234,6 @@ __device__ __forceinline__ void prefill_item(const ps_attn_launch a, int item, P
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) o[rt][t] = mfma32(av[t], pb[rt], o[rt][t], DT{});
                 }
-                constexpr uint32_t one2 = std::is_same<DT, TBF16>::value ? 0x3F803F80u : 0x3C003C00u;
-                const u32x4 ones = {one2, one2, one2, one2};
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) o[rt][NTL - 1] = mfma32(ones, pb[rt], o[rt][NTL - 1], DT{});
             }
